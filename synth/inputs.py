@@ -1,0 +1,147 @@
+"""Seeded input generators and the five workload shapes.
+
+Every tensor draws from ``numpy.random.default_rng([2026, cfg, tensor_id])``
+or, for a [B, T, D] sequence tensor, from one generator per block of
+``T_BLOCK`` time steps, ``default_rng([2026, cfg, tensor_id, tb])``, so that any
+slice along T can be regenerated without drawing the whole tensor.  Values are
+drawn in float64 and rounded to float32 (round to nearest even); the bf16
+inputs are rounded once more, float32 -> bf16, again to nearest even.  The
+same rounded values feed the GPU library and the oracle.
+
+Large workloads whose host copy would be too heavy to draw in NumPy use
+``device_normal`` / ``device_uniform``: a seeded ``torch.Generator`` on the
+device.  Those values differ from the NumPy ones but follow the same
+distributions, and the oracle reads back whatever slice it checks.
+
+The shapes follow the pages' usage examples: a minGRU layer of width 512 on a
+(2, 1024, 512) batch (minGRU-pytorch profile, guide "Install and apply the
+minGRU layer") and a MinMax hidden state of d_state = 192 (minmaxrnc,
+"Custom configuration").
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+SEED_ROOT = 2026
+T_BLOCK = 512
+
+TENSOR_IDS = {
+    "x": 0,
+    "W_in": 1,
+    "W_out": 2,
+    "h0": 3,
+    "k": 4,
+    "p": 5,
+    "r": 6,
+    "s": 7,
+    "x0": 8,
+}
+
+# The five workloads (config index = position + 1).  "N(0, 1/D)" names a
+# variance, so the standard deviation is D ** -0.5.
+CONFIGS = {
+    1: dict(name="tiny_layer_fp32", kind="layer", B=2, T=64, D=16, dtype="f32",
+            w_std=16 ** -0.5, h0=False),
+    2: dict(name="layer_b2_t1024_d512_fp32", kind="layer", B=2, T=1024, D=512,
+            dtype="f32", w_std=512 ** -0.5, h0=False),
+    3: dict(name="scan_b8_t65536_d1024_bf16", kind="scan", B=8, T=65536,
+            D=1024, dtype="bf16", k_mean=-4.0, k_std=1.0, p_mean=0.0,
+            p_std=1.0, h0=True),
+    4: dict(name="step_b256_d2048_fp32", kind="step", B=256, D=2048,
+            T_prefill=512, steps=4096, dtype="f32", w_std=2048 ** -0.5),
+    5: dict(name="minmax_b8_t32768_d192_fp32", kind="minmax", B=8, T=32768,
+            D=192, dtype="f32"),
+}
+
+
+def _rng(cfg: int, name: str, tb: int | None = None) -> np.random.Generator:
+    key = [SEED_ROOT, int(cfg), TENSOR_IDS[name]]
+    if tb is not None:
+        key.append(int(tb))
+    return np.random.default_rng(key)
+
+
+def bf16_round(a: np.ndarray) -> torch.Tensor:
+    """float32 array -> bf16 tensor, round to nearest even (torch's cast)."""
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16)
+
+
+def _no_negative_zero(a: np.ndarray) -> np.ndarray:
+    # A drawn -0.0 becomes +0.0 so that min/max ties never hinge on the sign
+    # of zero.
+    a[a == 0] = 0.0
+    return a
+
+
+def normal_bt(cfg: int, name: str, B: int, T: int, D: int, mean: float = 0.0,
+              std: float = 1.0, t0: int = 0) -> np.ndarray:
+    """float32 [B, T, D] sequence tensor ~ N(mean, std^2), drawn per T-block.
+
+    ``t0`` must be a multiple of T_BLOCK; the slice [t0, t0 + T) is returned.
+    """
+    if t0 % T_BLOCK:
+        raise ValueError("t0 must be a multiple of T_BLOCK")
+    out = np.empty((B, T, D), dtype=np.float32)
+    tb0 = t0 // T_BLOCK
+    nb = -(-T // T_BLOCK)
+    for i in range(nb):
+        lo = i * T_BLOCK
+        n = min(T_BLOCK, T - lo)
+        blk = _rng(cfg, name, tb0 + i).standard_normal((B, T_BLOCK, D))
+        out[:, lo:lo + n, :] = (mean + std * blk[:, :n, :]).astype(np.float32)
+    return out
+
+
+def uniform_bt(cfg: int, name: str, B: int, T: int, D: int, lo: float,
+               hi: float, t0: int = 0) -> np.ndarray:
+    """float32 [B, T, D] ~ U(lo, hi) per T-block, no negative zeros."""
+    if t0 % T_BLOCK:
+        raise ValueError("t0 must be a multiple of T_BLOCK")
+    out = np.empty((B, T, D), dtype=np.float32)
+    tb0 = t0 // T_BLOCK
+    nb = -(-T // T_BLOCK)
+    for i in range(nb):
+        a = i * T_BLOCK
+        n = min(T_BLOCK, T - a)
+        blk = _rng(cfg, name, tb0 + i).uniform(lo, hi, (B, T_BLOCK, D))
+        out[:, a:a + n, :] = blk[:, :n, :].astype(np.float32)
+    return _no_negative_zero(out)
+
+
+def normal_mat(cfg: int, name: str, rows: int, cols: int, std: float) -> np.ndarray:
+    """float32 weight matrix ~ N(0, std^2)."""
+    return (std * _rng(cfg, name).standard_normal((rows, cols))).astype(np.float32)
+
+
+def normal_vec(cfg: int, name: str, B: int, D: int, mean: float = 0.0,
+               std: float = 1.0) -> np.ndarray:
+    """float32 [B, D] state ~ N(mean, std^2)."""
+    return (mean + std * _rng(cfg, name).standard_normal((B, D))).astype(np.float32)
+
+
+def uniform_vec(cfg: int, name: str, B: int, D: int, lo: float, hi: float) -> np.ndarray:
+    return _no_negative_zero(_rng(cfg, name).uniform(lo, hi, (B, D)).astype(np.float32))
+
+
+def _torch_gen(cfg: int, name: str, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(SEED_ROOT * 1_000_003 + int(cfg) * 1009 + TENSOR_IDS[name])
+    return g
+
+
+def device_normal(cfg: int, name: str, shape, mean: float = 0.0, std: float = 1.0,
+                  dtype=torch.float32, device="cuda") -> torch.Tensor:
+    """Seeded N(mean, std^2) drawn on ``device`` in float32, then cast to dtype."""
+    t = torch.empty(shape, dtype=torch.float32, device=device)
+    t.normal_(mean, std, generator=_torch_gen(cfg, name, device))
+    return t.to(dtype) if dtype != torch.float32 else t
+
+
+def device_uniform(cfg: int, name: str, shape, lo: float, hi: float,
+                   device="cuda") -> torch.Tensor:
+    """Seeded U(lo, hi) float32 on ``device``, no negative zeros."""
+    t = torch.empty(shape, dtype=torch.float32, device=device)
+    t.uniform_(lo, hi, generator=_torch_gen(cfg, name, device))
+    return t.masked_fill_(t == 0, 0.0)
