@@ -1,0 +1,300 @@
+#!/usr/bin/env python3
+"""Benchmark of the gfx950 minGRU log-space scan (and its sibling paths).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs c3,c5,c4,c2,c1]
+
+One step is one pass of the scan hot path over one batch: the headline
+workload is the long-sequence scan B=8, T=65536, D=1024 with bf16 gate logits
+k and candidate pre-activations p, an fp32 carried state h0 and fp32 outputs
+h and h_T (the fused activation -> log-space coefficient transform, the
+in-register / LDS / look-back scan and the apply + store, all in one launch
+after a small workspace reset).  Inputs are seeded synthetic tensors drawn on
+the GPU and resident in HBM before the timed region.  The printed JSON line
+carries:
+
+* value      -- elements (B*T*D) per second over the K timed steps;
+* roofline   -- algorithmic bytes per launch (8 B per element plus h0 and
+                h_T) over the average launch duration measured with HIP
+                events on the launch stream, against the 8 TB/s HBM peak;
+                ``traffic`` comes from committed rocprofv3 counter runs when
+                they were taken on the current kernel source, else null;
+* cpu_baseline -- the fp64 CPU oracle timed on a bounded sample of the same
+                workload (every channel, a prefix of the sequence);
+* legs       -- the other measurements: the MinMax scan, the decode-style
+                step loop, the small layers, and a device copy ceiling.
+
+Only one GPU is used; --gpus above 1 exits with a message.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("scan elements/s (B·T·D) + achieved HBM GB/s vs peak, "
+          "minGRU log-space scan")
+HBM_PEAK_GBPS = 8000.0
+FP32_MFMA_PEAK_TFLOPS = 157.3
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_b8_t65536_d1024_bf16_traffic.json")
+SCAN_SOURCE = os.path.join(ROOT, "scan_linear_rnn_amd", "csrc", "scan.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash(path=SCAN_SOURCE) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def time_launches(torch, fn, steps, warmup):
+    """Runs fn `warmup` times, then `steps` times bracketed by synchronisation.
+    Returns (wall seconds for the K steps, mean per-launch ms from HIP events
+    recorded on the current stream around each launch)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record()
+        fn()
+        ends[i].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return wall, sum(per) / len(per), min(per)
+
+
+def leg_c3(torch, sr, synth, steps, warmup, cpu_steps):
+    import ctypes
+    cfg = synth.CONFIGS[3]
+    B, T, D = cfg["B"], cfg["T"], cfg["D"]
+    log(f"[bench] c3 scan B={B} T={T} D={D}: generating inputs")
+    kb = synth.device_normal(3, "k", (B, T, D), cfg["k_mean"], cfg["k_std"], torch.bfloat16)
+    pb = synth.device_normal(3, "p", (B, T, D), cfg["p_mean"], cfg["p_std"], torch.bfloat16)
+    h0 = synth.device_normal(3, "h0", (B, D))
+    y = torch.empty((B, T, D), dtype=torch.float32, device="cuda")
+    last = torch.empty((B, D), dtype=torch.float32, device="cuda")
+    lib = sr.raw_library()
+    nbytes = lib.mingru_forward_workspace_size(B, T, 0, D, D, 0, 0)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    args = (B, T, 0, D, D, None, None, ctypes.c_void_p(kb.data_ptr()),
+            ctypes.c_void_p(pb.data_ptr()), D, sr.SR_BF16, ctypes.c_void_p(h0.data_ptr()), None,
+            ctypes.c_void_p(y.data_ptr()), ctypes.c_void_p(last.data_ptr()),
+            ctypes.c_void_p(ws.data_ptr()), nbytes, stream)
+
+    def step():
+        st = lib.mingru_forward(*args)
+        if st:
+            raise RuntimeError(lib.scanrnn_last_error().decode())
+
+    log(f"[bench] c3: {warmup} warmup + {steps} timed steps")
+    wall, mean_ms, min_ms = time_launches(torch, step, steps, warmup)
+    if sr.workspace_status(ws) != 0:
+        raise RuntimeError("look-back wait expired during the benchmark")
+    if not bool(torch.isfinite(y).all()):
+        raise RuntimeError("non-finite scan output")
+    n = B * T * D
+    alg_bytes = n * (2 + 2 + 4) + 2 * B * D * 4
+    ach = alg_bytes / (mean_ms * 1e-3) / 1e9
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("kernel_source_sha256_16") == source_hash():
+            traffic = tr.get("bytes_per_launch")
+    res = dict(
+        B=B, T=T, D=D, elements=n, wall_s=wall, ms_per_step=wall / steps * 1e3,
+        launch_ms_mean=mean_ms, launch_ms_min=min_ms,
+        value=n / (wall / steps),
+        roofline={"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
+                  "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                  "alg_bytes_per_launch": alg_bytes,
+                  "kernel": "chunk_scan_kernel<MinGRUOp, bf16, V=2> (+ workspace reset)"},
+    )
+    if cpu_steps > 0:
+        log(f"[bench] c3: CPU oracle on every channel, first {cpu_steps} steps")
+        from oracle import mingru
+        ks = kb[:, :cpu_steps].double().cpu().numpy()
+        ps = pb[:, :cpu_steps].double().cpu().numpy()
+        hs = h0.double().cpu().numpy()
+        t0 = time.perf_counter()
+        mingru.scan(ks, ps, hs)
+        dt = time.perf_counter() - t0
+        ns = B * cpu_steps * D
+        res["cpu_baseline"] = {
+            "value": ns / dt, "unit": "elements/s", "cores": 1, "kind": "oracle",
+            "sample": f"all {B}x{D} channels, steps [0, {cpu_steps}) of T={T} "
+                      f"({ns} elements, {dt:.1f} s; NumPy fp64 sequential loop, one thread)",
+        }
+    del kb, pb, y, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def leg_c5(torch, sr, synth, steps, warmup):
+    cfg = synth.CONFIGS[5]
+    B, T, D = cfg["B"], cfg["T"], cfg["D"]
+    log(f"[bench] c5 minmax B={B} T={T} D={D}")
+    r = synth.device_uniform(5, "r", (B, T, D), -1.0, 1.0)
+    s = synth.device_uniform(5, "s", (B, T, D), -1.5, 0.5)
+    x0 = synth.device_uniform(5, "x0", (B, D), -1.0, 1.0)
+    out = torch.empty_like(r)
+    last = torch.empty((B, D), device="cuda")
+    ws = torch.empty(sr.raw_library().minmax_scan_workspace_size(B, T, D), dtype=torch.uint8,
+                     device="cuda")
+
+    def step():
+        sr.minmax_scan(r, s, x0, return_last=True, workspace=ws, out=out, out_last=last)
+
+    wall, mean_ms, min_ms = time_launches(torch, step, steps, warmup)
+    n = B * T * D
+    alg = n * 12 + 2 * B * D * 4
+    return dict(B=B, T=T, D=D, elements_per_s=n / (wall / steps), launch_ms_mean=mean_ms,
+                achieved_GBps=alg / (mean_ms * 1e-3) / 1e9,
+                frac_of_hbm_peak=alg / (mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS)
+
+
+def leg_c4(torch, sr, synth, n_steps):
+    cfg = synth.CONFIGS[4]
+    B, D, Tp = cfg["B"], cfg["D"], cfg["T_prefill"]
+    log(f"[bench] c4 prefill B={B} T={Tp} D={D}, then {n_steps} steps")
+    W_in = synth.device_normal(4, "W_in", (D, 2 * D), 0.0, cfg["w_std"])
+    W_out = synth.device_normal(4, "W_out", (D, D), 0.0, cfg["w_std"])
+    x = synth.device_normal(4, "x", (B, Tp + n_steps, D))
+    torch.cuda.synchronize()
+    # Prefill (parallel forward over 512 steps), timed on its own.
+    y, h = sr.mingru_forward(x[:, :Tp], W_in, W_out=W_out, return_last=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    y, h = sr.mingru_forward(x[:, :Tp], W_in, W_out=W_out, return_last=True)
+    torch.cuda.synchronize()
+    t_prefill = time.perf_counter() - t0
+    prefill_flops = 2.0 * B * Tp * D * (2 * D) + 2.0 * B * Tp * D * D
+    xs = [x[:, Tp + t].contiguous() for t in range(n_steps)]
+    yt = None
+    hh = h.clone()
+    for t in range(3):
+        yt, hh = sr.mingru_step(xs[t], W_in, W_out, h_prev=hh, h_next=hh)
+    hh = h.clone()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for t in range(n_steps):
+        yt, hh = sr.mingru_step(xs[t], W_in, W_out, h_prev=hh, h_next=hh)
+    torch.cuda.synchronize()
+    t_steps = time.perf_counter() - t0
+    step_flops = 2.0 * B * D * (2 * D) + 2.0 * B * D * D
+    return dict(B=B, D=D, prefill_T=Tp, prefill_ms=t_prefill * 1e3,
+                prefill_TFLOPs=prefill_flops / t_prefill / 1e12,
+                prefill_frac_fp32_mfma=prefill_flops / t_prefill / 1e12 / FP32_MFMA_PEAK_TFLOPS,
+                steps=n_steps, steps_per_s=n_steps / t_steps,
+                step_us=t_steps / n_steps * 1e6,
+                step_TFLOPs=step_flops * n_steps / t_steps / 1e12,
+                step_frac_fp32_mfma=step_flops * n_steps / t_steps / 1e12 / FP32_MFMA_PEAK_TFLOPS)
+
+
+def leg_layer(torch, sr, synth, cfg_id, steps):
+    cfg = synth.CONFIGS[cfg_id]
+    B, T, D = cfg["B"], cfg["T"], cfg["D"]
+    x = synth.device_normal(cfg_id, "x", (B, T, D))
+    W_in = synth.device_normal(cfg_id, "W_in", (D, 2 * D), 0.0, cfg["w_std"])
+    W_out = synth.device_normal(cfg_id, "W_out", (D, D), 0.0, cfg["w_std"])
+    wall, mean_ms, _ = time_launches(torch, lambda: sr.mingru_forward(x, W_in, W_out=W_out),
+                                     steps, 3)
+    res = dict(B=B, T=T, D=D, forward_ms=wall / steps * 1e3, forward_launch_ms=mean_ms,
+               elements_per_s=B * T * D / (wall / steps))
+    xs = [x[:, t].contiguous() for t in range(T)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    h = None
+    for t in range(T):
+        _, h = sr.mingru_step(xs[t], W_in, W_out, h_prev=h)
+    torch.cuda.synchronize()
+    res["step_loop_ms"] = (time.perf_counter() - t0) * 1e3
+    res["steps_per_s"] = T / (time.perf_counter() - t0)
+    return res
+
+
+def leg_copy(torch):
+    n = 1 << 29  # 2 GiB of fp32, the size of the scan's output
+    a = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    wall, mean_ms, _ = time_launches(torch, lambda: b.copy_(a), 10, 3)
+    del a, b
+    torch.cuda.empty_cache()
+    return dict(bytes_per_copy=2 * 4 * n, GBps=2 * 4 * n / (mean_ms * 1e-3) / 1e9)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[1])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--legs", default="c3,c5,c4,c2,c1,copy")
+    ap.add_argument("--cpu-steps", type=int, default=16384,
+                    help="sequence prefix the CPU oracle baseline runs over (0 = skip)")
+    ap.add_argument("--c4-steps", type=int, default=4096)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import scan_linear_rnn_amd as sr
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    legs = [s.strip() for s in args.legs.split(",") if s.strip()]
+    out = {"metric": METRIC}
+    extra = {}
+    c3 = None
+    if "c3" in legs:
+        c3 = leg_c3(torch, sr, synth, args.steps, args.warmup, args.cpu_steps)
+    if "copy" in legs:
+        extra["copy_ceiling"] = leg_copy(torch)
+    if "c5" in legs:
+        extra["minmax_b8_t32768_d192"] = leg_c5(torch, sr, synth, args.steps, args.warmup)
+    if "c2" in legs:
+        extra["layer_b2_t1024_d512"] = leg_layer(torch, sr, synth, 2, 10)
+    if "c1" in legs:
+        extra["layer_b2_t64_d16"] = leg_layer(torch, sr, synth, 1, 10)
+    if "c4" in legs:
+        extra["step_b256_d2048"] = leg_c4(torch, sr, synth, args.c4_steps)
+    if c3 is not None:
+        out.update({
+            "value": c3["value"], "unit": "elements/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": c3["ms_per_step"], "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": "minGRU log-space scan, B=8 T=65536 D=1024, bf16 k/p inputs, "
+                                   "fp32 h0/h/h_T", "B": c3["B"], "T": c3["T"], "D": c3["D"],
+                       "inputs": "bf16", "parallelism": "single GPU"},
+            "roofline": c3["roofline"],
+        })
+        if "cpu_baseline" in c3:
+            out["cpu_baseline"] = c3["cpu_baseline"]
+        extra["scan_launch_ms_mean"] = c3["launch_ms_mean"]
+        extra["scan_launch_ms_min"] = c3["launch_ms_min"]
+        if "copy_ceiling" in extra:
+            out["roofline"]["frac_of_copy_ceiling"] = round(
+                out["roofline"]["achieved"] / extra["copy_ceiling"]["GBps"], 4)
+    out["legs"] = extra
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

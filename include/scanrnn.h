@@ -1,0 +1,152 @@
+/*
+ * scanrnn.h -- C ABI of the MI355X (gfx950) minGRU / MinMax scan library.
+ *
+ * What the calls compute
+ * ----------------------
+ * minGRU layer (the log-space minGRU layer profiled on openvist.com as
+ * "Mingru Pytorch"; intro and "Requirements & limits": a log-space numerically
+ * stable layer with a parallel mode and a token-by-token mode that carries the
+ * hidden state):
+ *
+ *     [k_t | p_t] = x_t W_in                 (k: first D_h columns, p: next D_h)
+ *     z_t = sigma(k_t),   htilde_t = g(p_t),  g(v) = v + 1/2 (v >= 0), sigma(v) (v < 0)
+ *     h_t = (1 - z_t) h_{t-1} + z_t htilde_t       t = 1..T, h_0 carried (absent = 0)
+ *     y_t = h_t W_out                        (absent W_out: y_t = h_t)
+ *
+ * evaluated with log(1 - z) = -softplus(k) and log z + log g(p) as the
+ * coefficients of an associative scan over t.
+ *
+ * MinMax neuron (minmaxrnc PyPI page, "The model" item 3):
+ *
+ *     x_{t+1} = max(min(r_t, x_t), s_t)   element-wise, by a prefix scan.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - All tensor pointers are DEVICE pointers; the caller owns every buffer,
+ *   including the workspace.  The library keeps no pointer after a call
+ *   returns and holds no global mutable state except a thread-local error
+ *   string.
+ * - Tensors are row-major, innermost (feature) dimension fastest; a [B,T,D]
+ *   tensor is B*T rows of D elements.  Pointers must be aligned to their
+ *   element size; wider alignment (8 or 16 bytes) lets the library use
+ *   vector loads.
+ * - Sizes are int64.  B*T*D may exceed 2^31; offsets are computed in 64 bits.
+ * - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *   stream).  Buffers must stay alive until the enqueued work completes.
+ * - Arguments are validated before anything is enqueued: on any non-OK status
+ *   nothing was launched and no output was written.  A failed HIP launch
+ *   returns SR_ERR_HIP.  scanrnn_last_error() gives the text of the last
+ *   non-OK status on the calling thread.  No C++ exception crosses the ABI.
+ * - Calls are reentrant; concurrent calls must use distinct workspaces.
+ * - Workspace: at least *_workspace_size(...) bytes, 256-byte aligned,
+ *   contents need not be initialised (the call resets what it uses, on the
+ *   stream, before the scan).
+ * - Determinism: minmax_scan is bit-exact (min and max only select).  The
+ *   minGRU calls agree with the sequential definition within rounding; the
+ *   order in which partial results are combined does not depend on timing,
+ *   so repeated calls give identical bits.
+ */
+#ifndef SCANRNN_H
+#define SCANRNN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SR_OK = 0,
+  SR_ERR_INVALID_ARGUMENT = 1,   /* null pointer, negative size, bad stride     */
+  SR_ERR_UNSUPPORTED = 2,        /* valid request this build does not handle    */
+  SR_ERR_WORKSPACE_TOO_SMALL = 3,
+  SR_ERR_HIP = 4,                /* a HIP runtime call failed                   */
+  SR_ERR_LOOKBACK_TIMEOUT = 5    /* reported by scanrnn_workspace_status only   */
+} sr_status;
+
+typedef enum { SR_F32 = 0, SR_BF16 = 1 } sr_dtype;
+
+/* Bytes of workspace mingru_forward needs.  has_w_in / has_w_out say whether
+ * the call will pass W_in / W_out (the projections need staging buffers:
+ * B*T*2*D_h floats for [k|p], B*T*D_h floats for h). */
+size_t mingru_forward_workspace_size(int64_t B, int64_t T, int64_t D_in, int64_t D_h,
+                                     int64_t D_out, int has_w_in, int has_w_out);
+
+/*
+ * Parallel mode: the whole sequence at once (minGRU profile, guide "Install
+ * and apply the minGRU layer": the output has the input's shape).
+ *
+ *   x      [B,T,D_in] fp32; read only when W_in != NULL.
+ *   W_in   [D_in, 2*D_h] fp32, or NULL: then k and p are given directly
+ *          (scan-only use) and x must be NULL.
+ *   k, p   rows of the pre-projected gate logits / candidate pre-activations,
+ *          element (b,t,d) at k[(b*T + t)*ld_kp + d]; dtype kp_dtype
+ *          (SR_F32 or SR_BF16).  ld_kp >= D_h, so k and p may be the two
+ *          halves of one [B,T,2*D_h] buffer.  Used only when W_in == NULL.
+ *   h0     [B,D_h] fp32 carried state, or NULL (zero state).
+ *   W_out  [D_h, D_out] fp32, or NULL (then D_out must equal D_h, y = h).
+ *   y      [B,T,D_out] fp32 output.
+ *   h_last [B,D_h] fp32, or NULL: receives h_T (h0, or zeros, when T == 0).
+ */
+sr_status mingru_forward(int64_t B, int64_t T, int64_t D_in, int64_t D_h, int64_t D_out,
+                         const float* x, const float* W_in,
+                         const void* k, const void* p, int64_t ld_kp, sr_dtype kp_dtype,
+                         const float* h0, const float* W_out,
+                         float* y, float* h_last,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace mingru_step needs. */
+size_t mingru_step_workspace_size(int64_t B, int64_t D_in, int64_t D_h, int64_t D_out);
+
+/*
+ * Sequential mode, one token (minGRU profile, guide "Process a sequence
+ * sequentially with carried hidden state"; the minGRU tutorial's Step 3: the
+ * base step returns the new hidden state, which is also its output).
+ *
+ *   x_t    [B,D_in] fp32;  W_in [D_in,2*D_h] fp32 (required).
+ *   W_out  [D_h,D_out] fp32 or NULL (then D_out must equal D_h).
+ *   h_prev [B,D_h] fp32 or NULL (zero state).
+ *   h_next [B,D_h] fp32; may be the same buffer as h_prev.
+ *   y_t    [B,D_out] fp32, or NULL when W_out is NULL (the output is h_next;
+ *          a non-NULL y_t then receives a copy).
+ */
+sr_status mingru_step(int64_t B, int64_t D_in, int64_t D_h, int64_t D_out,
+                      const float* x_t, const float* W_in, const float* W_out,
+                      const float* h_prev, float* h_next, float* y_t,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace minmax_scan needs. */
+size_t minmax_scan_workspace_size(int64_t B, int64_t T, int64_t D);
+
+/*
+ * MinMax neuron over a sequence (minmaxrnc PyPI page, "The model" item 3;
+ * "Quick start" carries the state across calls).
+ *
+ *   r, s   [B,T,D] fp32 inputs of steps t = 0..T-1.
+ *   x0     [B,D] fp32 initial state (required).
+ *   x_out  [B,T,D] fp32: x_out[:,t,:] = x_{t+1}.
+ *   x_last [B,D] fp32 or NULL: receives x_T (x0 when T == 0).
+ * Results are bit-exact; NaN inputs are outside the contract.
+ */
+sr_status minmax_scan(int64_t B, int64_t T, int64_t D,
+                      const float* r, const float* s, const float* x0,
+                      float* x_out, float* x_last,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Text of the last non-OK status returned on this thread ("" if none). */
+const char* scanrnn_last_error(void);
+
+/* Waits for `stream`, then reports whether a scan that used `workspace` since
+ * its last reset gave up waiting for a predecessor chunk (a bounded wait that
+ * should never expire; SR_ERR_LOOKBACK_TIMEOUT if it did, SR_OK otherwise). */
+sr_status scanrnn_workspace_status(const void* workspace, void* stream);
+
+/* Library version, "major.minor.patch". */
+const char* scanrnn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SCANRNN_H */

@@ -1,0 +1,324 @@
+"""Python binding of libscanrnn.so, the gfx950 minGRU / MinMax scan library.
+
+The calls carry the C ABI's names (include/scanrnn.h) and only marshal
+arguments: they check devices, dtypes and shapes, allocate outputs and the
+workspace through PyTorch's caching allocator, and pass raw device pointers
+and PyTorch's current HIP stream to the library.  Every step of the
+computation runs in the library's HIP kernels; there is no other code path.
+If the shared library is missing the import fails loudly.
+
+    from scan_linear_rnn_amd import MinGRU, mingru_forward, mingru_step, minmax_scan
+
+The layer object follows the minGRU profile's usage (guide "Install and apply
+the minGRU layer": a layer of width 512 applied to a (2, 1024, 512) batch
+returns the same shape; guide "Process a sequence sequentially": per token,
+pass the previous hidden state -- None at first -- with
+return_next_prev_hidden=True and keep the returned state).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "MinGRU",
+    "mingru_forward",
+    "mingru_step",
+    "minmax_scan",
+    "library_path",
+    "ScanRNNError",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libscanrnn.so")
+
+SR_OK = 0
+SR_ERR_INVALID_ARGUMENT = 1
+SR_ERR_UNSUPPORTED = 2
+SR_ERR_WORKSPACE_TOO_SMALL = 3
+SR_ERR_HIP = 4
+SR_ERR_LOOKBACK_TIMEOUT = 5
+SR_F32 = 0
+SR_BF16 = 1
+
+EXPORTED = (
+    "mingru_forward_workspace_size",
+    "mingru_forward",
+    "mingru_step_workspace_size",
+    "mingru_step",
+    "minmax_scan_workspace_size",
+    "minmax_scan",
+    "scanrnn_last_error",
+    "scanrnn_workspace_status",
+    "scanrnn_version",
+)
+
+
+class ScanRNNError(RuntimeError):
+    def __init__(self, fn: str, status: int, message: str):
+        super().__init__(f"{fn} failed with status {status}: {message}")
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            f"{_LIB_PATH} is missing: build the HIP library first "
+            "(python -m scan_linear_rnn_amd.build)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    i64, sz, vp, i32 = ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int
+    lib.mingru_forward_workspace_size.restype = sz
+    lib.mingru_forward_workspace_size.argtypes = [i64, i64, i64, i64, i64, i32, i32]
+    lib.mingru_forward.restype = i32
+    lib.mingru_forward.argtypes = [i64, i64, i64, i64, i64, vp, vp, vp, vp, i64, i32, vp, vp,
+                                   vp, vp, vp, sz, vp]
+    lib.mingru_step_workspace_size.restype = sz
+    lib.mingru_step_workspace_size.argtypes = [i64, i64, i64, i64]
+    lib.mingru_step.restype = i32
+    lib.mingru_step.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.minmax_scan_workspace_size.restype = sz
+    lib.minmax_scan_workspace_size.argtypes = [i64, i64, i64]
+    lib.minmax_scan.restype = i32
+    lib.minmax_scan.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.scanrnn_last_error.restype = ctypes.c_char_p
+    lib.scanrnn_last_error.argtypes = []
+    lib.scanrnn_workspace_status.restype = i32
+    lib.scanrnn_workspace_status.argtypes = [vp, vp]
+    lib.scanrnn_version.restype = ctypes.c_char_p
+    lib.scanrnn_version.argtypes = []
+    return lib
+
+
+_lib = _load()
+
+
+def raw_library() -> ctypes.CDLL:
+    """The loaded ctypes library (for ABI-level tests)."""
+    return _lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != SR_OK:
+        msg = _lib.scanrnn_last_error().decode(errors="replace")
+        raise ScanRNNError(fn, status, msg)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=torch.float32, ndim=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims (got shape {tuple(t.shape)})")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    return t.contiguous()
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def mingru_forward(x=None, W_in=None, *, k=None, p=None, h0=None, W_out=None,
+                   return_last=False, workspace=None, out=None, out_last=None):
+    """Parallel mode over a whole sequence.
+
+    Either ``x`` [B,T,D_in] with ``W_in`` [D_in, 2*D_h], or the pre-projected
+    ``k``, ``p`` ([B,T,D_h], fp32 or bf16, or two halves of one [B,T,2*D_h]
+    buffer).  ``h0`` [B,D_h] is the carried state (None = zero), ``W_out``
+    [D_h, D_out] the output projection (None = identity).  Returns y
+    [B,T,D_out] fp32, and h_T [B,D_h] when ``return_last``.
+    """
+    if W_in is not None:
+        x = _dev(x, "x", ndim=3)
+        W_in = _dev(W_in, "W_in", ndim=2)
+        B, T, D_in = x.shape
+        if W_in.shape[0] != D_in or W_in.shape[1] % 2:
+            raise ValueError(f"W_in must be [{D_in}, 2*D_h] (got {tuple(W_in.shape)})")
+        D_h = W_in.shape[1] // 2
+        device = x.device
+        kk = pp = None
+        ld_kp, kp_dtype = 0, SR_F32
+    else:
+        if x is not None:
+            raise ValueError("pass either x with W_in, or k and p")
+        if k is None or p is None:
+            raise ValueError("k and p are required when W_in is None")
+        if k.dtype not in (torch.float32, torch.bfloat16) or p.dtype != k.dtype:
+            raise TypeError("k and p must both be float32 or both bfloat16")
+        if k.device.type != "cuda" or p.device != k.device:
+            raise ValueError("k and p must be on the same GPU")
+        if k.dim() != 3 or p.shape != k.shape:
+            raise ValueError("k and p must be [B,T,D_h] of the same shape")
+        B, T, D_h = k.shape
+        D_in = 0
+        device = k.device
+        # Rows may be strided (two halves of one buffer); the feature dim must
+        # be unit-stride and both must share one row stride.
+        if (k.stride(2) != 1 or p.stride(2) != 1 or k.stride(0) != T * k.stride(1)
+                or p.stride(1) != k.stride(1) or p.stride(0) != k.stride(0)):
+            k = k.contiguous()
+            p = p.contiguous()
+        ld_kp = k.stride(1)
+        kp_dtype = SR_BF16 if k.dtype == torch.bfloat16 else SR_F32
+        kk, pp = k, p
+    if h0 is not None:
+        h0 = _dev(h0, "h0", shape=(B, D_h))
+    if W_out is not None:
+        W_out = _dev(W_out, "W_out", ndim=2)
+        if W_out.shape[0] != D_h:
+            raise ValueError(f"W_out must be [{D_h}, D_out] (got {tuple(W_out.shape)})")
+        D_out = W_out.shape[1]
+    else:
+        D_out = D_h
+    if out is not None:
+        if not out.is_contiguous():
+            raise ValueError("out must be contiguous")
+        y = _dev(out, "out", shape=(B, T, D_out))
+    else:
+        y = torch.empty((B, T, D_out), dtype=torch.float32, device=device)
+    h_last = None
+    if return_last:
+        if out_last is not None:
+            if not out_last.is_contiguous():
+                raise ValueError("out_last must be contiguous")
+            h_last = _dev(out_last, "out_last", shape=(B, D_h))
+        else:
+            h_last = torch.empty((B, D_h), dtype=torch.float32, device=device)
+    nbytes = _lib.mingru_forward_workspace_size(B, T, D_in, D_h, D_out, int(W_in is not None),
+                                                int(W_out is not None))
+    ws = workspace if workspace is not None and workspace.numel() >= nbytes else _workspace(nbytes, device)
+    st = _lib.mingru_forward(B, T, D_in, D_h, D_out, _ptr(x if W_in is not None else None),
+                             _ptr(W_in), _ptr(kk), _ptr(pp), ld_kp, kp_dtype, _ptr(h0),
+                             _ptr(W_out), _ptr(y), _ptr(h_last), _ptr(ws), ws.numel(),
+                             _stream(device))
+    _check("mingru_forward", st)
+    return (y, h_last) if return_last else y
+
+
+def mingru_step(x_t, W_in, W_out=None, h_prev=None, h_next=None):
+    """Sequential mode, one token: x_t [B,D_in] -> (y_t [B,D_out], h_t [B,D_h]).
+
+    ``h_prev`` None is the zero state.  ``h_next`` may be given (it may be the
+    same tensor as ``h_prev``) to avoid an allocation.  Without ``W_out`` the
+    output is the new hidden state itself (the same tensor is returned twice).
+    """
+    x_t = _dev(x_t, "x_t", ndim=2)
+    W_in = _dev(W_in, "W_in", ndim=2)
+    B, D_in = x_t.shape
+    if W_in.shape[0] != D_in or W_in.shape[1] % 2:
+        raise ValueError(f"W_in must be [{D_in}, 2*D_h] (got {tuple(W_in.shape)})")
+    D_h = W_in.shape[1] // 2
+    device = x_t.device
+    if h_prev is not None:
+        if not h_prev.is_contiguous():
+            raise ValueError("h_prev must be contiguous")
+        h_prev = _dev(h_prev, "h_prev", shape=(B, D_h))
+    if h_next is None:
+        h_next = torch.empty((B, D_h), dtype=torch.float32, device=device)
+    else:
+        if not h_next.is_contiguous():
+            raise ValueError("h_next must be contiguous")
+        _dev(h_next, "h_next", shape=(B, D_h))
+    if W_out is not None:
+        W_out = _dev(W_out, "W_out", ndim=2)
+        if W_out.shape[0] != D_h:
+            raise ValueError(f"W_out must be [{D_h}, D_out] (got {tuple(W_out.shape)})")
+        D_out = W_out.shape[1]
+        y_t = torch.empty((B, D_out), dtype=torch.float32, device=device)
+    else:
+        D_out = D_h
+        y_t = None
+    st = _lib.mingru_step(B, D_in, D_h, D_out, _ptr(x_t), _ptr(W_in), _ptr(W_out), _ptr(h_prev),
+                          _ptr(h_next), _ptr(y_t), None, 0, _stream(device))
+    _check("mingru_step", st)
+    return (h_next if y_t is None else y_t), h_next
+
+
+def minmax_scan(r, s, x0, return_last=False, workspace=None, out=None, out_last=None):
+    """MinMax neuron x_{t+1} = max(min(r_t, x_t), s_t) over [B,T,D] inputs.
+
+    Returns x_out [B,T,D] (x_out[:, t] = x_{t+1}), and x_T when ``return_last``.
+    """
+    r = _dev(r, "r", ndim=3)
+    s = _dev(s, "s", shape=r.shape)
+    B, T, D = r.shape
+    x0 = _dev(x0, "x0", shape=(B, D))
+    if out is not None:
+        if not out.is_contiguous():
+            raise ValueError("out must be contiguous")
+        out = _dev(out, "out", shape=(B, T, D))
+    else:
+        out = torch.empty_like(r)
+    last = None
+    if return_last:
+        if out_last is not None:
+            if not out_last.is_contiguous():
+                raise ValueError("out_last must be contiguous")
+            last = _dev(out_last, "out_last", shape=(B, D))
+        else:
+            last = torch.empty((B, D), dtype=torch.float32, device=r.device)
+    nbytes = _lib.minmax_scan_workspace_size(B, T, D)
+    ws = workspace if workspace is not None and workspace.numel() >= nbytes else _workspace(nbytes, r.device)
+    st = _lib.minmax_scan(B, T, D, _ptr(r), _ptr(s), _ptr(x0), _ptr(out), _ptr(last), _ptr(ws),
+                          ws.numel(), _stream(r.device))
+    _check("minmax_scan", st)
+    return (out, last) if return_last else out
+
+
+def workspace_status(ws: torch.Tensor) -> int:
+    """Synchronises the current stream and returns the workspace status code."""
+    return _lib.scanrnn_workspace_status(_ptr(ws), _stream(ws.device))
+
+
+class MinGRU:
+    """A minGRU layer: W_in [dim, 2*dim*expansion], W_out [dim*expansion, dim].
+
+    ``layer(x)`` with x [B,T,dim] runs the parallel mode and returns y of the
+    same shape.  ``layer(x_t, prev_hidden, return_next_prev_hidden=True)`` with
+    a single token (x_t [B,dim] or [B,1,dim]) runs one step and returns
+    (y_t, h_t); prev_hidden None is the zero state.
+    """
+
+    def __init__(self, dim: int, expansion: float = 1.0, W_in=None, W_out=None,
+                 device="cuda", generator=None):
+        self.dim = int(dim)
+        self.dim_inner = int(dim * expansion)
+        if W_in is None:
+            W_in = torch.randn(self.dim, 2 * self.dim_inner, generator=generator) / self.dim ** 0.5
+        if W_out is None:
+            W_out = torch.randn(self.dim_inner, self.dim, generator=generator) / self.dim_inner ** 0.5
+        self.W_in = W_in.to(device=device, dtype=torch.float32).contiguous()
+        self.W_out = None if W_out is False else W_out.to(device=device, dtype=torch.float32).contiguous()
+
+    def __call__(self, x, prev_hidden=None, return_next_prev_hidden=False):
+        single = x.dim() == 2 or (x.dim() == 3 and x.shape[1] == 1 and prev_hidden is not None)
+        if single:
+            x_t = x.reshape(x.shape[0], x.shape[-1])
+            h = None if prev_hidden is None else prev_hidden.reshape(x_t.shape[0], self.dim_inner)
+            y_t, h_t = mingru_step(x_t, self.W_in, self.W_out, h)
+            if x.dim() == 3:
+                y_t = y_t.unsqueeze(1)
+            return (y_t, h_t) if return_next_prev_hidden else y_t
+        h0 = None
+        if prev_hidden is not None:
+            h0 = prev_hidden.reshape(x.shape[0], self.dim_inner)
+        y, h_last = mingru_forward(x, self.W_in, h0=h0, W_out=self.W_out, return_last=True)
+        return (y, h_last) if return_next_prev_hidden else y

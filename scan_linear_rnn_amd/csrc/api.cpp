@@ -1,0 +1,253 @@
+// C ABI entry points: argument validation, workspace carving, launches.
+//
+// Every check runs before anything is enqueued, so a non-OK status means
+// nothing was launched and no output was touched.  No HIP call is made on a
+// validation failure, which also lets the checks run on a machine without a
+// GPU.
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "internal.hpp"
+
+namespace sr {
+
+namespace {
+thread_local char g_last_error[512] = "";
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_mul_overflow(a, b, out); }
+
+// n = a * b * c without overflow, all non-negative.
+bool prod3(int64_t a, int64_t b, int64_t c, int64_t* n) {
+  int64_t ab;
+  return mul_ok(a, b, &ab) && mul_ok(ab, c, n);
+}
+
+bool aligned(const void* p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+struct FwdLayout {
+  size_t scan_bytes, kp_off, kp_bytes, h_off, h_bytes, total;
+};
+
+FwdLayout forward_layout(int64_t B, int64_t T, int64_t D_h, bool w_in, bool w_out) {
+  FwdLayout L{};
+  L.scan_bytes = align_up(scan_workspace_bytes(B, T, D_h), kAlign);
+  L.kp_off = L.scan_bytes;
+  L.kp_bytes = w_in ? align_up(size_t(B) * size_t(T) * size_t(2 * D_h) * 4, kAlign) : 0;
+  L.h_off = L.kp_off + L.kp_bytes;
+  L.h_bytes = w_out ? align_up(size_t(B) * size_t(T) * size_t(D_h) * 4, kAlign) : 0;
+  L.total = L.h_off + L.h_bytes;
+  return L;
+}
+
+sr_status check_workspace(void* ws, size_t have, size_t need) {
+  if (need == 0) return SR_OK;
+  if (ws == nullptr) return fail(SR_ERR_INVALID_ARGUMENT, "workspace is NULL (%zu bytes needed)", need);
+  if (!aligned(ws, kAlign)) return fail(SR_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  if (have < need)
+    return fail(SR_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, %zu needed", have, need);
+  return SR_OK;
+}
+
+#define SR_REQUIRE(cond, ...)                                   \
+  do {                                                          \
+    if (!(cond)) return fail(SR_ERR_INVALID_ARGUMENT, __VA_ARGS__); \
+  } while (0)
+
+}  // namespace
+
+sr_status fail(sr_status code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+}  // namespace sr
+
+using namespace sr;
+
+extern "C" {
+
+const char* scanrnn_last_error(void) { return g_last_error; }
+
+const char* scanrnn_version(void) { return "0.1.0"; }
+
+size_t mingru_forward_workspace_size(int64_t B, int64_t T, int64_t D_in, int64_t D_h,
+                                     int64_t D_out, int has_w_in, int has_w_out) {
+  (void)D_in;
+  (void)D_out;
+  int64_t n;
+  if (B < 0 || T < 0 || D_h < 0 || !prod3(B, T, 2 * D_h, &n)) return 0;
+  return forward_layout(B, T, D_h, has_w_in != 0, has_w_out != 0).total;
+}
+
+sr_status mingru_forward(int64_t B, int64_t T, int64_t D_in, int64_t D_h, int64_t D_out,
+                         const float* x, const float* W_in, const void* k, const void* p,
+                         int64_t ld_kp, sr_dtype kp_dtype, const float* h0, const float* W_out,
+                         float* y, float* h_last, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  g_last_error[0] = '\0';
+  SR_REQUIRE(B >= 0 && T >= 0 && D_in >= 0 && D_h >= 0 && D_out >= 0,
+             "sizes must be non-negative (B=%lld T=%lld D_in=%lld D_h=%lld D_out=%lld)",
+             (long long)B, (long long)T, (long long)D_in, (long long)D_h, (long long)D_out);
+  int64_t n_kp, n_x, n_y, n_h;
+  SR_REQUIRE(prod3(B, T, 2 * D_h, &n_kp) && prod3(B, T, D_in, &n_x) && prod3(B, T, D_out, &n_y) &&
+                 prod3(B, T, D_h, &n_h),
+             "tensor sizes overflow int64");
+  const bool w_in = W_in != nullptr, w_out = W_out != nullptr;
+  if (!w_out)
+    SR_REQUIRE(D_out == D_h, "without W_out the output width D_out (%lld) must equal D_h (%lld)",
+               (long long)D_out, (long long)D_h);
+  SR_REQUIRE(n_y == 0 || y != nullptr, "y is NULL");
+  SR_REQUIRE(aligned(y, 4) && aligned(h0, 4) && aligned(h_last, 4) && aligned(W_out, 4) &&
+                 aligned(W_in, 4) && aligned(x, 4),
+             "fp32 pointers must be 4-byte aligned");
+  if (w_in) {
+    SR_REQUIRE(k == nullptr && p == nullptr, "with W_in the projected k and p must be NULL");
+    SR_REQUIRE(n_x == 0 || x != nullptr, "x is NULL while W_in is given");
+  } else {
+    SR_REQUIRE(x == nullptr, "x must be NULL when W_in is NULL (pass k and p instead)");
+    SR_REQUIRE(kp_dtype == SR_F32 || kp_dtype == SR_BF16, "kp_dtype %d unsupported", int(kp_dtype));
+    SR_REQUIRE(n_h == 0 || (k != nullptr && p != nullptr), "k or p is NULL");
+    SR_REQUIRE(ld_kp >= D_h, "ld_kp (%lld) must be >= D_h (%lld)", (long long)ld_kp, (long long)D_h);
+    const size_t esz = kp_dtype == SR_BF16 ? 2 : 4;
+    SR_REQUIRE(aligned(k, esz) && aligned(p, esz), "k and p must be aligned to their element size");
+    int64_t span;
+    SR_REQUIRE(prod3(B, T, ld_kp, &span), "k/p extent overflows int64");
+  }
+  const FwdLayout L = forward_layout(B, T, D_h, w_in, w_out);
+  sr_status st = check_workspace(workspace, workspace_bytes, L.total);
+  if (st != SR_OK) return st;
+
+  hipStream_t s = as_stream(stream);
+  char* ws = static_cast<char*>(workspace);
+  float* kp_buf = w_in ? reinterpret_cast<float*>(ws + L.kp_off) : nullptr;
+  float* h_buf = w_out ? reinterpret_cast<float*>(ws + L.h_off) : y;
+
+  if (B == 0 || D_h == 0) {
+    // No channels: y has no elements unless D_out > 0 with W_out (then y = 0).
+    if (w_out && n_y > 0) return launch_copy_or_zero(y, nullptr, n_y, s);
+    return SR_OK;
+  }
+  if (w_in && T > 0) {
+    st = launch_gemm_f32(B * T, 2 * D_h, D_in, x, D_in, W_in, 2 * D_h, kp_buf, 2 * D_h, s);
+    if (st != SR_OK) return st;
+  }
+  ScanRequest rq{};
+  rq.op = ScanOp::kMinGRU;
+  rq.in_dtype = w_in ? SR_F32 : kp_dtype;
+  rq.B = B;
+  rq.T = T;
+  rq.D = D_h;
+  rq.in0 = w_in ? static_cast<const void*>(kp_buf) : k;
+  rq.in1 = w_in ? static_cast<const void*>(kp_buf + D_h) : p;
+  rq.ld_in = w_in ? 2 * D_h : ld_kp;
+  rq.init = h0;
+  rq.out = h_buf;
+  rq.last = h_last;
+  rq.workspace = ws;
+  rq.stream = s;
+  st = launch_scan(rq);
+  if (st != SR_OK) return st;
+  if (w_out && T > 0) st = launch_gemm_f32(B * T, D_out, D_h, h_buf, D_h, W_out, D_out, y, D_out, s);
+  return st;
+}
+
+size_t mingru_step_workspace_size(int64_t B, int64_t D_in, int64_t D_h, int64_t D_out) {
+  (void)B;
+  (void)D_in;
+  (void)D_h;
+  (void)D_out;
+  return 0;
+}
+
+sr_status mingru_step(int64_t B, int64_t D_in, int64_t D_h, int64_t D_out, const float* x_t,
+                      const float* W_in, const float* W_out, const float* h_prev, float* h_next,
+                      float* y_t, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error[0] = '\0';
+  (void)workspace;
+  (void)workspace_bytes;
+  SR_REQUIRE(B >= 0 && D_in >= 0 && D_h >= 0 && D_out >= 0,
+             "sizes must be non-negative (B=%lld D_in=%lld D_h=%lld D_out=%lld)", (long long)B,
+             (long long)D_in, (long long)D_h, (long long)D_out);
+  int64_t n_x, n_h, n_y, n_w;
+  SR_REQUIRE(prod3(B, D_in, 1, &n_x) && prod3(B, D_h, 1, &n_h) && prod3(B, D_out, 1, &n_y) &&
+                 prod3(D_in, 2 * D_h, 1, &n_w),
+             "tensor sizes overflow int64");
+  SR_REQUIRE(W_in != nullptr || n_w == 0, "W_in is NULL");
+  SR_REQUIRE(x_t != nullptr || n_x == 0, "x_t is NULL");
+  SR_REQUIRE(h_next != nullptr || n_h == 0, "h_next is NULL");
+  if (W_out == nullptr)
+    SR_REQUIRE(D_out == D_h, "without W_out the output width D_out (%lld) must equal D_h (%lld)",
+               (long long)D_out, (long long)D_h);
+  else
+    SR_REQUIRE(y_t != nullptr || n_y == 0, "y_t is NULL while W_out is given");
+  SR_REQUIRE(aligned(x_t, 4) && aligned(W_in, 4) && aligned(W_out, 4) && aligned(h_prev, 4) &&
+                 aligned(h_next, 4) && aligned(y_t, 4),
+             "fp32 pointers must be 4-byte aligned");
+  if (B == 0) return SR_OK;
+  hipStream_t s = as_stream(stream);
+  sr_status st = launch_step_in(B, D_in, D_h, x_t, W_in, h_prev, h_next, s);
+  if (st != SR_OK) return st;
+  if (W_out != nullptr) return launch_gemm_f32(B, D_out, D_h, h_next, D_h, W_out, D_out, y_t, D_out, s);
+  if (y_t != nullptr && y_t != h_next) return launch_copy_or_zero(y_t, h_next, n_h, s);
+  return SR_OK;
+}
+
+size_t minmax_scan_workspace_size(int64_t B, int64_t T, int64_t D) {
+  int64_t n;
+  if (B < 0 || T < 0 || D < 0 || !prod3(B, T, D, &n)) return 0;
+  return align_up(scan_workspace_bytes(B, T, D), kAlign);
+}
+
+sr_status minmax_scan(int64_t B, int64_t T, int64_t D, const float* r, const float* s,
+                      const float* x0, float* x_out, float* x_last, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  g_last_error[0] = '\0';
+  SR_REQUIRE(B >= 0 && T >= 0 && D >= 0, "sizes must be non-negative (B=%lld T=%lld D=%lld)",
+             (long long)B, (long long)T, (long long)D);
+  int64_t n, nbd;
+  SR_REQUIRE(prod3(B, T, D, &n) && prod3(B, D, 1, &nbd), "tensor sizes overflow int64");
+  SR_REQUIRE(n == 0 || (r != nullptr && s != nullptr && x_out != nullptr), "r, s or x_out is NULL");
+  SR_REQUIRE(nbd == 0 || x0 != nullptr, "x0 is required");
+  SR_REQUIRE(aligned(r, 4) && aligned(s, 4) && aligned(x0, 4) && aligned(x_out, 4) &&
+                 aligned(x_last, 4),
+             "fp32 pointers must be 4-byte aligned");
+  sr_status st = check_workspace(workspace, workspace_bytes, minmax_scan_workspace_size(B, T, D));
+  if (st != SR_OK) return st;
+  ScanRequest rq{};
+  rq.op = ScanOp::kMinMax;
+  rq.in_dtype = SR_F32;
+  rq.B = B;
+  rq.T = T;
+  rq.D = D;
+  rq.in0 = r;
+  rq.in1 = s;
+  rq.ld_in = D;
+  rq.init = x0;
+  rq.out = x_out;
+  rq.last = x_last;
+  rq.workspace = workspace;
+  rq.stream = as_stream(stream);
+  return launch_scan(rq);
+}
+
+sr_status scanrnn_workspace_status(const void* workspace, void* stream) {
+  g_last_error[0] = '\0';
+  SR_REQUIRE(workspace != nullptr, "workspace is NULL");
+  uint32_t flag = 0;
+  hipStream_t s = as_stream(stream);
+  hipError_t err = hipMemcpyAsync(&flag, static_cast<const char*>(workspace) + 4, 4,
+                                  hipMemcpyDeviceToHost, s);
+  if (err == hipSuccess) err = hipStreamSynchronize(s);
+  if (err != hipSuccess) return fail(SR_ERR_HIP, "reading workspace status: %s", hipGetErrorString(err));
+  if (flag != 0) return fail(SR_ERR_LOOKBACK_TIMEOUT, "a scan gave up waiting for a predecessor tile");
+  return SR_OK;
+}
+
+}  // extern "C"

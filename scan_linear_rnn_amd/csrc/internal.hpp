@@ -1,0 +1,77 @@
+// Internal declarations shared by the host API and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "scanrnn.h"
+
+namespace sr {
+
+// Records a printf-style message as the calling thread's last error and
+// returns `code`.
+sr_status fail(sr_status code, const char* fmt, ...);
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+constexpr size_t kAlign = 256;
+
+// ---------------------------------------------------------------- scan engine
+//
+// The workspace of one scan: a 256-byte header (ticket counter, status word)
+// followed by one 64-bit state word per (chunk along T, batch row, channel).
+
+struct ScanGeometry {
+  int V;             // channels per lane
+  int N;             // time steps per lane
+  int W;             // waves per workgroup (stacked along T)
+  int64_t Dc;        // channels per workgroup = 64 * V
+  int64_t Tc;        // time steps per workgroup = W * N
+  int64_t n_dtiles;  // ceil(D / Dc)
+  int64_t n_tchunks; // ceil(T / Tc)
+};
+
+// Largest workspace any geometry needs for a [B,T,D] scan.
+size_t scan_workspace_bytes(int64_t B, int64_t T, int64_t D);
+
+enum class ScanOp { kMinGRU, kMinMax };
+
+struct ScanRequest {
+  ScanOp op;
+  sr_dtype in_dtype;   // k,p (minGRU) or r,s (MinMax, fp32 only)
+  int64_t B, T, D;
+  const void* in0;     // k or r
+  const void* in1;     // p or s
+  int64_t ld_in;       // row stride of in0/in1, elements
+  const float* init;   // h0 / x0 [B,D] or nullptr (zero state)
+  float* out;          // [B,T,D] contiguous
+  float* last;         // [B,D] or nullptr
+  void* workspace;
+  hipStream_t stream;
+};
+
+sr_status launch_scan(const ScanRequest& rq);
+
+// Chooses the geometry a request will use (exposed for sizing and tests).
+ScanGeometry choose_geometry(const ScanRequest& rq);
+
+// ---------------------------------------------------------------- GEMM
+//
+// C[M,N] = A[M,K] * B[K,N], fp32, row-major with leading dimensions.
+sr_status launch_gemm_f32(int64_t M, int64_t N, int64_t K,
+                          const float* A, int64_t lda,
+                          const float* Bm, int64_t ldb,
+                          float* C, int64_t ldc, hipStream_t stream);
+
+// Step kernel: h_next = h_prev + z * (g(p) - h_prev) with [k|p] = x_t W_in,
+// computed as one GEMM whose epilogue applies the update.
+sr_status launch_step_in(int64_t Bsz, int64_t D_in, int64_t D_h,
+                         const float* x_t, const float* W_in,
+                         const float* h_prev, float* h_next, hipStream_t stream);
+
+// Copies n floats (src may be null: writes zeros).
+sr_status launch_copy_or_zero(float* dst, const float* src, int64_t n, hipStream_t stream);
+
+}  // namespace sr

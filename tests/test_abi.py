@@ -1,0 +1,120 @@
+"""The C ABI: the shared library loads, exports every function the header
+declares, sizes workspaces, and rejects bad arguments before launching
+anything (so these run without a GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "scanrnn.h")
+
+sr = pytest.importorskip("scan_linear_rnn_amd")
+lib = sr.raw_library()
+
+FAKE = ctypes.c_void_p(0x10000)      # never dereferenced: validation fails first
+FAKE2 = ctypes.c_void_p(0x20000)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+
+
+def test_header_declares_the_expected_calls():
+    names = set(declared_functions())
+    assert names == set(sr.EXPORTED), names
+
+
+@pytest.mark.parametrize("name", declared_functions())
+def test_every_declared_symbol_is_exported(name):
+    assert hasattr(lib, name), name
+    assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_version_and_empty_error():
+    assert lib.scanrnn_version().decode().count(".") == 2
+    assert isinstance(lib.scanrnn_last_error(), bytes)
+
+
+def test_workspace_sizes():
+    # Scan-only forward needs only the look-back words; projections add the
+    # staging buffers for [k|p] and h.
+    s0 = lib.mingru_forward_workspace_size(8, 65536, 0, 1024, 1024, 0, 0)
+    s1 = lib.mingru_forward_workspace_size(8, 65536, 1024, 1024, 1024, 1, 0)
+    s2 = lib.mingru_forward_workspace_size(8, 65536, 1024, 1024, 1024, 1, 1)
+    assert 0 < s0 < 2 ** 27
+    assert s1 - s0 >= 8 * 65536 * 2048 * 4
+    assert s2 - s1 >= 8 * 65536 * 1024 * 4
+    assert all(v % 256 == 0 for v in (s0, s1, s2))
+    assert lib.minmax_scan_workspace_size(8, 32768, 192) > 0
+    assert lib.mingru_forward_workspace_size(-1, 4, 4, 4, 4, 0, 0) == 0
+    assert lib.mingru_step_workspace_size(256, 2048, 2048, 2048) == 0
+
+
+def _fwd(**kw):
+    args = dict(B=2, T=8, D_in=0, D_h=4, D_out=4, x=None, W_in=None, k=FAKE, p=FAKE2,
+                ld_kp=4, kp_dtype=sr.SR_F32, h0=None, W_out=None, y=FAKE, h_last=None,
+                ws=FAKE, ws_bytes=1 << 30, stream=None)
+    args.update(kw)
+    return lib.mingru_forward(args["B"], args["T"], args["D_in"], args["D_h"], args["D_out"],
+                              args["x"], args["W_in"], args["k"], args["p"], args["ld_kp"],
+                              args["kp_dtype"], args["h0"], args["W_out"], args["y"],
+                              args["h_last"], args["ws"], args["ws_bytes"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=-1), sr.SR_ERR_INVALID_ARGUMENT),
+    (dict(T=-3), sr.SR_ERR_INVALID_ARGUMENT),
+    (dict(y=None), sr.SR_ERR_INVALID_ARGUMENT),
+    (dict(k=None), sr.SR_ERR_INVALID_ARGUMENT),
+    (dict(ld_kp=3), sr.SR_ERR_INVALID_ARGUMENT),
+    (dict(kp_dtype=7), sr.SR_ERR_INVALID_ARGUMENT),
+    (dict(D_out=5), sr.SR_ERR_INVALID_ARGUMENT),
+    (dict(x=FAKE), sr.SR_ERR_INVALID_ARGUMENT),
+    (dict(W_in=FAKE), sr.SR_ERR_INVALID_ARGUMENT),        # k, p must then be NULL
+    (dict(y=ctypes.c_void_p(0x10002)), sr.SR_ERR_INVALID_ARGUMENT),
+    (dict(k=ctypes.c_void_p(0x10001), kp_dtype=1), sr.SR_ERR_INVALID_ARGUMENT),
+    (dict(ws=None), sr.SR_ERR_INVALID_ARGUMENT),
+    (dict(ws=ctypes.c_void_p(0x10040)), sr.SR_ERR_INVALID_ARGUMENT),
+    (dict(ws_bytes=16), sr.SR_ERR_WORKSPACE_TOO_SMALL),
+    (dict(B=1 << 40, T=1 << 40), sr.SR_ERR_INVALID_ARGUMENT),
+])
+def test_forward_rejects_bad_arguments(kw, code):
+    assert _fwd(**kw) == code
+    assert lib.scanrnn_last_error()
+
+
+def test_step_rejects_bad_arguments():
+    f = lib.mingru_step
+    assert f(-1, 4, 4, 4, FAKE, FAKE, None, None, FAKE, None, None, 0, None) == sr.SR_ERR_INVALID_ARGUMENT
+    assert f(2, 4, 4, 4, FAKE, None, None, None, FAKE, None, None, 0, None) == sr.SR_ERR_INVALID_ARGUMENT
+    assert f(2, 4, 4, 3, FAKE, FAKE, None, None, FAKE, None, None, 0, None) == sr.SR_ERR_INVALID_ARGUMENT
+    assert f(2, 4, 4, 3, FAKE, FAKE, FAKE, None, FAKE, None, None, 0, None) == sr.SR_ERR_INVALID_ARGUMENT
+    assert f(2, 4, 4, 4, FAKE, FAKE, None, None, None, None, None, 0, None) == sr.SR_ERR_INVALID_ARGUMENT
+
+
+def test_minmax_rejects_bad_arguments():
+    f = lib.minmax_scan
+    big = 1 << 30
+    assert f(2, 8, 4, FAKE, FAKE, None, FAKE, None, FAKE, big, None) == sr.SR_ERR_INVALID_ARGUMENT
+    assert f(2, 8, 4, None, FAKE, FAKE, FAKE, None, FAKE, big, None) == sr.SR_ERR_INVALID_ARGUMENT
+    assert f(2, 8, -4, FAKE, FAKE, FAKE, FAKE, None, FAKE, big, None) == sr.SR_ERR_INVALID_ARGUMENT
+    assert f(2, 8, 4, FAKE, FAKE, FAKE, FAKE, None, FAKE, 8, None) == sr.SR_ERR_WORKSPACE_TOO_SMALL
+    assert f(2, 8, 4, FAKE, FAKE, FAKE, FAKE, None, None, big, None) == sr.SR_ERR_INVALID_ARGUMENT
+
+
+def test_status_requires_workspace():
+    assert lib.scanrnn_workspace_status(None, None) == sr.SR_ERR_INVALID_ARGUMENT
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(2, 8, 4)
+    with pytest.raises(ValueError):
+        sr.minmax_scan(x, x, torch.zeros(2, 4))
+    with pytest.raises((ValueError, TypeError)):
+        sr.mingru_forward(k=x, p=x)

@@ -1,0 +1,86 @@
+"""GPU parity of the MinMax scan: bit for bit against the sequential oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import metrics, minmax
+from tests.gpu_util import dev, say
+
+pytestmark = pytest.mark.gpu
+
+sr = pytest.importorskip("scan_linear_rnn_amd")
+
+
+def _inputs(B, T, D, seed):
+    rng = np.random.default_rng([600, seed])
+    r = rng.uniform(-1, 1, (B, T, D)).astype(np.float32)
+    s = (rng.uniform(-1, 1, (B, T, D)) - 0.5).astype(np.float32)
+    x0 = rng.uniform(-1, 1, (B, D)).astype(np.float32)
+    for a in (r, s, x0):
+        a[a == 0] = 0.0
+    return r, s, x0
+
+
+@pytest.mark.parametrize("B,T,D", [
+    (2, 64, 16), (3, 1000, 200), (1, 1, 5), (2, 5000, 192), (4, 3333, 7), (1, 40000, 64),
+])
+def test_minmax_bitwise(B, T, D):
+    say(f"minmax B={B} T={T} D={D}")
+    r, s, x0 = _inputs(B, T, D, seed=B + T + D)
+    out, last = sr.minmax_scan(dev(r), dev(s), dev(x0), return_last=True)
+    ref, ref_last = minmax.scan(r, s, x0)
+    assert metrics.bits_equal(out.cpu().numpy(), ref)
+    assert metrics.bits_equal(last.cpu().numpy(), ref_last)
+
+
+def test_minmax_full_c5_bitwise():
+    cfg = synth.CONFIGS[5]
+    B, T, D = cfg["B"], cfg["T"], cfg["D"]
+    say("minmax full C5")
+    r = synth.uniform_bt(5, "r", B, T, D, -1.0, 1.0)
+    s = synth.uniform_bt(5, "s", B, T, D, -1.0, 1.0) - np.float32(0.5)
+    s[s == 0] = 0.0
+    x0 = synth.uniform_vec(5, "x0", B, D, -1.0, 1.0)
+    out, last = sr.minmax_scan(dev(r), dev(s), dev(x0), return_last=True)
+    ref, ref_last = minmax.scan(r, s, x0)
+    assert metrics.bits_equal(out.cpu().numpy(), ref)
+    assert metrics.bits_equal(last.cpu().numpy(), ref_last)
+
+
+def test_minmax_hold_and_single_reset_across_tiles():
+    B, T, D = 2, 30000, 192
+    rng = np.random.default_rng(601)
+    r = np.full((B, T, D), 2.0, np.float32)
+    s = np.full((B, T, D), -2.0, np.float32)
+    x0 = rng.uniform(-1, 1, (B, D)).astype(np.float32)
+    out = sr.minmax_scan(dev(r), dev(s), dev(x0)).cpu().numpy()
+    assert np.array_equal(out, np.broadcast_to(x0[:, None, :], out.shape))
+    tstar = 17777
+    v = rng.uniform(-1.5, 1.5, (B, D)).astype(np.float32)
+    r[:, tstar] = -3.0
+    s[:, tstar] = v
+    out = sr.minmax_scan(dev(r), dev(s), dev(x0)).cpu().numpy()
+    assert np.array_equal(out[:, :tstar], np.broadcast_to(x0[:, None, :], (B, tstar, D)))
+    assert np.array_equal(out[:, tstar:], np.broadcast_to(v[:, None, :], (B, T - tstar, D)))
+
+
+def test_minmax_repeated_and_split_calls_identical():
+    B, T, D = 3, 9000, 192
+    r, s, x0 = _inputs(B, T, D, seed=602)
+    rd, sd, xd = dev(r), dev(s), dev(x0)
+    full, last = sr.minmax_scan(rd, sd, xd, return_last=True)
+    for _ in range(2):
+        assert torch.equal(sr.minmax_scan(rd, sd, xd), full)
+    T1 = 4321
+    a, la = sr.minmax_scan(rd[:, :T1].contiguous(), sd[:, :T1].contiguous(), xd, return_last=True)
+    b, lb = sr.minmax_scan(rd[:, T1:].contiguous(), sd[:, T1:].contiguous(), la, return_last=True)
+    assert torch.equal(torch.cat([a, b], dim=1), full) and torch.equal(lb, last)
+
+
+def test_minmax_empty_sequence():
+    x0 = dev(np.float32([[0.5, -0.25]]))
+    e = torch.zeros((1, 0, 2), device="cuda")
+    out, last = sr.minmax_scan(e, e, x0, return_last=True)
+    assert out.shape == (1, 0, 2) and torch.equal(last, x0)
