@@ -26,11 +26,14 @@
 //   * Phase 1 (all waves): each lane loads its N x V inputs, turns them into
 //     maps (the fused activation -> coefficient transform), keeps the maps in
 //     registers and composes them into one map per channel.
-//   * Phase 2 (wave 0): the W per-wave maps meet in LDS; wave 0 forms each
-//     wave's exclusive prefix and the tile's map, publishes the tile's map,
-//     then looks back along T through the tiles before it (decoupled
-//     look-back) until it finds one that published its end state, and
-//     publishes this tile's end state in turn.
+//   * Phase 2 (one thread per channel): the W per-wave maps meet in LDS and
+//     give each wave's exclusive prefix and the tile's map, which is
+//     published.  Then all threads fetch, in one round trip, the look-back
+//     words of the preceding tiles of the same channels into LDS (decoupled
+//     look-back with a window); the nearest published end state, followed by
+//     the maps of the tiles after it, gives the state entering the tile.
+//     Only if the window holds no usable end state does the thread walk back
+//     one tile at a time.  The tile's end state is then published.
 //   * Phase 3 (all waves): each lane starts from the state entering its run
 //     and re-applies its register-resident maps, storing h (or x) per step.
 //
@@ -65,6 +68,7 @@ constexpr uint32_t kSpinLimit = 1u << 20;
 constexpr size_t kHeaderBytes = 256;
 constexpr int kWaves = 8;            // waves per workgroup
 constexpr int kElemsPerLane = 32;    // N * V: maps each lane keeps in registers
+constexpr int kWindowWords = 2048;   // look-back words fetched per round trip (16 KiB)
 
 struct Pair {
   float u, v;
@@ -108,64 +112,73 @@ struct MinMaxOp {
 
 // ------------------------------------------------------------------ loads
 
-// Raw vector of V inputs as loaded from memory, and its conversion to float.
+// Buffer resources: a 128-bit descriptor (base, byte extent) lets a wave
+// address its rows with one per-lane byte offset plus a per-row scalar
+// offset, instead of a 64-bit address per load; reads past the extent return
+// zero instead of faulting.  Word 3 is the gfx9-family raw-buffer format.
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int64_t n = bytes <= 0 ? 0 : (bytes > int64_t(0xFFFFFFFF) ? int64_t(0xFFFFFFFF) : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(uint32_t(n)), kRsrcWord3);
+}
+
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// V inputs of type TIn as loaded (raw bits), and their conversion to float.
 template <typename TIn, int V> struct Raw;
 
 template <> struct Raw<uint16_t, 1> {  // bf16
-  using type = uint16_t;
-  static __device__ __forceinline__ void unpack(type r, float (&f)[1]) {
-    f[0] = __uint_as_float(uint32_t(r) << 16);
+  using type = uint32_t;
+  static __device__ __forceinline__ type load(rsrc_t r, int voff, int soff) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+  }
+  static __device__ __forceinline__ void unpack(type x, float (&f)[1]) {
+    f[0] = __uint_as_float(x << 16);
   }
 };
 template <> struct Raw<uint16_t, 2> {
   using type = uint32_t;
-  static __device__ __forceinline__ void unpack(type r, float (&f)[2]) {
-    f[0] = __uint_as_float(r << 16);
-    f[1] = __uint_as_float(r & 0xFFFF0000u);
+  static __device__ __forceinline__ type load(rsrc_t r, int voff, int soff) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
   }
-};
-template <> struct Raw<uint16_t, 4> {
-  using type = uint2;
-  static __device__ __forceinline__ void unpack(type r, float (&f)[4]) {
-    f[0] = __uint_as_float(r.x << 16);
-    f[1] = __uint_as_float(r.x & 0xFFFF0000u);
-    f[2] = __uint_as_float(r.y << 16);
-    f[3] = __uint_as_float(r.y & 0xFFFF0000u);
+  static __device__ __forceinline__ void unpack(type x, float (&f)[2]) {
+    f[0] = __uint_as_float(x << 16);
+    f[1] = __uint_as_float(x & 0xFFFF0000u);
   }
 };
 template <> struct Raw<float, 1> {
-  using type = float;
-  static __device__ __forceinline__ void unpack(type r, float (&f)[1]) { f[0] = r; }
+  using type = uint32_t;
+  static __device__ __forceinline__ type load(rsrc_t r, int voff, int soff) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+  }
+  static __device__ __forceinline__ void unpack(type x, float (&f)[1]) { f[0] = __uint_as_float(x); }
 };
 template <> struct Raw<float, 2> {
-  using type = float2;
-  static __device__ __forceinline__ void unpack(type r, float (&f)[2]) {
-    f[0] = r.x;
-    f[1] = r.y;
+  using type = u32x2;
+  static __device__ __forceinline__ type load(rsrc_t r, int voff, int soff) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
   }
-};
-template <> struct Raw<float, 4> {
-  using type = float4;
-  static __device__ __forceinline__ void unpack(type r, float (&f)[4]) {
-    f[0] = r.x;
-    f[1] = r.y;
-    f[2] = r.z;
-    f[3] = r.w;
+  static __device__ __forceinline__ void unpack(type x, float (&f)[2]) {
+    f[0] = __uint_as_float(x.x);
+    f[1] = __uint_as_float(x.y);
   }
 };
 
 template <int V> struct OutVec;
 template <> struct OutVec<1> {
-  static __device__ __forceinline__ void store(float* p, const float (&h)[1]) { *p = h[0]; }
-};
-template <> struct OutVec<2> {
-  static __device__ __forceinline__ void store(float* p, const float (&h)[2]) {
-    *reinterpret_cast<float2*>(p) = make_float2(h[0], h[1]);
+  static __device__ __forceinline__ void store(rsrc_t r, int voff, int soff, const float (&h)[1]) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(h[0]), r, voff, soff, 0);
   }
 };
-template <> struct OutVec<4> {
-  static __device__ __forceinline__ void store(float* p, const float (&h)[4]) {
-    *reinterpret_cast<float4*>(p) = make_float4(h[0], h[1], h[2], h[3]);
+template <> struct OutVec<2> {
+  static __device__ __forceinline__ void store(rsrc_t r, int voff, int soff, const float (&h)[2]) {
+    u32x2 v;
+    v.x = __float_as_uint(h[0]);
+    v.y = __float_as_uint(h[1]);
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, voff, soff, 0);
   }
 };
 
@@ -204,75 +217,43 @@ struct ScanParams {
   uint64_t* state;    // [n_tchunks][B][D] look-back words
 };
 
-// Wave 0's look-back for its V channels: returns the state entering tile
-// `tchunk` of batch row b.
-template <class Op, int V>
-__device__ __forceinline__ void lookback(const ScanParams& P, int64_t tchunk, int64_t b,
-                                         int64_t d, float (&hin)[V]) {
-  const size_t stride = size_t(P.B) * size_t(P.D);
+// Look-back along T for one channel, one tile at a time: used when the
+// window fetched in one round trip holds no usable end state.  Returns the
+// state entering tile `tchunk` of batch row b, channel d.
+template <class Op>
+__device__ float lookback_serial(const ScanParams& P, int64_t tchunk, int64_t b, int64_t d) {
+  const size_t plane = size_t(P.B) * size_t(P.D);
   const uint64_t* col = P.state + size_t(b) * size_t(P.D) + size_t(d);
-  int64_t i[V];
-  bool done[V];
-#pragma unroll
-  for (int c = 0; c < V; ++c) {
-    i[c] = tchunk - 1;
-    done[c] = false;
-    hin[c] = (P.init != nullptr) ? P.init[size_t(b) * P.D + d + c] : 0.0f;
-  }
+  float h = (P.init != nullptr) ? P.init[size_t(b) * P.D + d] : 0.0f;
   // Backward: find the nearest earlier tile whose end state is published.
+  int64_t i = tchunk - 1;
   uint32_t spins = 0;
-  bool timed_out = false;
-  while (true) {
-    bool all_done = true;
-    uint64_t w[V];
-#pragma unroll
-    for (int c = 0; c < V; ++c)
-      if (!done[c]) w[c] = load_word(col + size_t(i[c]) * stride + c);
-    bool waiting = false;
-#pragma unroll
-    for (int c = 0; c < V; ++c) {
-      if (done[c]) continue;
-      const uint32_t hi = uint32_t(w[c] >> 32);
-      if (hi == kTagState) {
-        hin[c] = __uint_as_float(uint32_t(w[c]));
-        done[c] = true;
-      } else if (hi != kTagEmpty) {
-        // A published map: step further back (tile 0 publishes only its
-        // state, so i never passes below 0; the guard keeps it that way).
-        if (--i[c] < 0) done[c] = true;  // hin keeps the initial state
-      } else {
-        waiting = true;
-      }
-      all_done = all_done && done[c];
+  while (i >= 0) {
+    const uint64_t w = load_word(col + size_t(i) * plane);
+    const uint32_t hi = uint32_t(w >> 32);
+    if (hi == kTagState) {
+      h = __uint_as_float(uint32_t(w));
+      break;
     }
-    if (all_done) break;
-    if (waiting) {
-      if (++spins > kSpinLimit) {
-        timed_out = true;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
+    if (hi != kTagEmpty) {
+      --i;  // a published map: keep walking (tile 0 publishes only its state)
+      continue;
     }
-  }
-  if (timed_out) {
-    __hip_atomic_store(P.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-    for (int c = 0; c < V; ++c) hin[c] = __uint_as_float(kCanonNaN);
-    return;
+    if (++spins > kSpinLimit) {
+      __hip_atomic_store(P.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return __uint_as_float(kCanonNaN);
+    }
+    __builtin_amdgcn_s_sleep(1);
   }
   // Forward: apply the maps of tiles i+1 .. tchunk-1 in order.
-#pragma unroll
-  for (int c = 0; c < V; ++c) {
-    float h = hin[c];
-    for (int64_t m = (i[c] < 0 ? 0 : i[c] + 1); m < tchunk; ++m) {
-      const uint64_t wm = load_word(col + size_t(m) * stride + c);
-      if (uint32_t(wm >> 32) == kTagState)
-        h = __uint_as_float(uint32_t(wm));  // tile m finished meanwhile: same value
-      else
-        h = Op::apply(unpack_map(wm), h);
-    }
-    hin[c] = h;
+  for (int64_t m = i + 1; m < tchunk; ++m) {
+    const uint64_t wm = load_word(col + size_t(m) * plane);
+    if (uint32_t(wm >> 32) == kTagState)
+      h = __uint_as_float(uint32_t(wm));  // tile m finished meanwhile: same value
+    else
+      h = Op::apply(unpack_map(wm), h);
   }
+  return h;
 }
 
 template <class Op, typename TIn, int V>
@@ -283,6 +264,7 @@ void chunk_scan_kernel(const ScanParams P) {
   using R = Raw<TIn, V>;
   __shared__ uint32_t s_ticket;
   __shared__ Pair s_pre[W][64 * V];
+  __shared__ uint64_t s_win[kWindowWords / (64 * V)][64 * V];
   __shared__ float s_hin[64 * V];
 
   const int lane = threadIdx.x & 63;
@@ -299,77 +281,123 @@ void chunk_scan_kernel(const ScanParams P) {
   const bool lane_on = d < P.D;
   const int64_t tw = tchunk * (W * N) + wave * N;  // first step of this wave's run
 
-  // Phase 1: load, transform, compose.  Loads outside the tensor are
-  // redirected to a valid element and their maps replaced by the identity,
-  // so the loads need no branches.
-  const TIn* in0 = static_cast<const TIn*>(P.in0);
-  const TIn* in1 = static_cast<const TIn*>(P.in1);
-  const int64_t dl = lane_on ? d : 0;
+  // Phase 1: load, transform, compose.  Loads need no branches: past the
+  // end of the tensor they return zero, and every map outside [0,T) x [0,D)
+  // is replaced by the identity.
+  // The wave's rows start at (b, tw); row n of the run is n*ld elements on.
+  const int64_t esz = sizeof(TIn);
+  const int64_t row0 = b * P.T + tw;
+  const int64_t dtile_first = int64_t(chain % n_dtiles) * (64 * V);
+  const int64_t base_el = row0 * P.ld_in + dtile_first;
+  const int64_t end_el = (P.B * P.T - 1) * P.ld_in + P.D;  // one past the last element
+  const rsrc_t r0 = make_rsrc(static_cast<const TIn*>(P.in0) + base_el, (end_el - base_el) * esz);
+  const rsrc_t r1 = make_rsrc(static_cast<const TIn*>(P.in1) + base_el, (end_el - base_el) * esz);
+  const int voff_in = int(lane * V * esz);
+  const int row_bytes = int(P.ld_in * esz);
   typename R::type raw0[N], raw1[N];
 #pragma unroll
   for (int n = 0; n < N; ++n) {
-    const int64_t t = (tw + n < P.T) ? tw + n : P.T - 1;
-    const size_t off = size_t(b * P.T + t) * size_t(P.ld_in) + size_t(dl);
-    raw0[n] = *reinterpret_cast<const typename R::type*>(in0 + off);
-    raw1[n] = *reinterpret_cast<const typename R::type*>(in1 + off);
+    raw0[n] = R::load(r0, voff_in, n * row_bytes);
+    raw1[n] = R::load(r1, voff_in, n * row_bytes);
   }
   Pair e[N][V];
   Pair agg[V];
 #pragma unroll
   for (int c = 0; c < V; ++c) agg[c] = Op::identity();
+  // Steps [0, nvalid) of the run lie inside the sequence (a wave-uniform
+  // bound, so the test is a scalar branch); lanes past D are reset below.
+  // Out-of-range maps are still replayed in phase 3 but never stored.
+  const int64_t rem = P.T - tw;
+  const int nvalid = rem <= 0 ? 0 : (rem >= N ? N : int(rem));
 #pragma unroll
   for (int n = 0; n < N; ++n) {
     float x0[V], x1[V];
     R::unpack(raw0[n], x0);
     R::unpack(raw1[n], x1);
-    const bool ok = lane_on && (tw + n < P.T);
 #pragma unroll
-    for (int c = 0; c < V; ++c) {
-      const Pair el = Op::element(x0[c], x1[c]);
-      e[n][c] = ok ? el : Op::identity();
-      agg[c] = Op::compose(agg[c], e[n][c]);
+    for (int c = 0; c < V; ++c) e[n][c] = Op::element(x0[c], x1[c]);
+    if (n < nvalid) {
+#pragma unroll
+      for (int c = 0; c < V; ++c) agg[c] = Op::compose(agg[c], e[n][c]);
     }
+    // Keep the scheduler from interleaving many steps' temporaries while
+    // all of the run's loads are still holding their registers.
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (!lane_on) {
+#pragma unroll
+    for (int c = 0; c < V; ++c) agg[c] = Op::identity();
   }
 #pragma unroll
   for (int c = 0; c < V; ++c) s_pre[wave][lane * V + c] = agg[c];
   __syncthreads();
 
-  // Phase 2: wave 0 combines the waves and looks back along T.
-  if (wave == 0) {
-    Pair run[V];
-#pragma unroll
-    for (int c = 0; c < V; ++c) run[c] = Op::identity();
+  // Phase 2: one thread per channel combines the waves' maps and resolves
+  // the state entering the tile.
+  constexpr int Dc = 64 * V;
+  constexpr int kWin = kWindowWords / Dc;  // predecessor tiles fetched at once
+  const int tid = threadIdx.x;
+  const int64_t dtile0 = int64_t(chain % n_dtiles) * Dc;
+  const bool chan_thread = tid < Dc;
+  const int64_t dc = dtile0 + tid;
+  const bool chan_on = chan_thread && dc < P.D;
+  const size_t plane = size_t(P.B) * size_t(P.D);  // words per tile index
+  Pair run = Op::identity();
+  if (chan_thread) {
 #pragma unroll
     for (int w = 0; w < W; ++w) {
-#pragma unroll
-      for (int c = 0; c < V; ++c) {
-        const Pair a = s_pre[w][lane * V + c];
-        s_pre[w][lane * V + c] = run[c];  // exclusive prefix of wave w
-        run[c] = Op::compose(run[c], a);
-      }
+      const Pair a = s_pre[w][tid];
+      s_pre[w][tid] = run;  // exclusive prefix of wave w
+      run = Op::compose(run, a);
     }
-    float hin[V];
-    uint64_t* slot = P.state + (size_t(tchunk) * size_t(P.B) + size_t(b)) * size_t(P.D) + size_t(d);
-    if (lane_on) {
-      if (tchunk == 0) {
-#pragma unroll
-        for (int c = 0; c < V; ++c)
-          hin[c] = (P.init != nullptr) ? P.init[size_t(b) * P.D + d + c] : 0.0f;
-      } else {
-#pragma unroll
-        for (int c = 0; c < V; ++c) store_word(slot + c, pack_map(run[c]));
-        lookback<Op, V>(P, tchunk, b, d, hin);
+  }
+  float hin = 0.0f;
+  if (tchunk == 0) {
+    if (chan_on && P.init != nullptr) hin = P.init[size_t(b) * P.D + dc];
+  } else {
+    if (chan_on) store_word(P.state + size_t(tchunk) * plane + size_t(b) * P.D + dc, pack_map(run));
+    // All threads fetch the words of the kWin preceding tiles into LDS in
+    // one round trip; position -1 stands for the initial state.
+    const int c = tid % Dc;
+    const int64_t dd = dtile0 + c;
+    for (int q = tid / Dc; q < kWin; q += (64 * W) / Dc) {
+      const int64_t m = tchunk - 1 - q;
+      uint64_t w = pack_state(__uint_as_float(kCanonNaN));
+      if (dd < P.D) {
+        if (m >= 0)
+          w = load_word(P.state + size_t(m) * plane + size_t(b) * P.D + dd);
+        else if (m == -1)
+          w = pack_state(P.init != nullptr ? P.init[size_t(b) * P.D + dd] : 0.0f);
       }
-      if (tchunk + 1 < P.n_tchunks) {
-#pragma unroll
-        for (int c = 0; c < V; ++c) store_word(slot + c, pack_state(Op::apply(run[c], hin[c])));
+      s_win[q][c] = w;
+    }
+  }
+  __syncthreads();
+  if (tchunk > 0 && chan_on) {
+    // Nearest published end state in the window, provided no tile between
+    // it and this one is still unwritten.
+    int found = -1;
+    for (int q = 0; q < kWin; ++q) {
+      const uint32_t hi = uint32_t(s_win[q][tid] >> 32);
+      if (hi == kTagState) {
+        found = q;
+        break;
       }
+      if (hi == kTagEmpty) break;
+    }
+    if (found >= 0) {
+      float h = __uint_as_float(uint32_t(s_win[found][tid]));
+      for (int q = found - 1; q >= 0; --q) h = Op::apply(unpack_map(s_win[q][tid]), h);
+      hin = h;
     } else {
-#pragma unroll
-      for (int c = 0; c < V; ++c) hin[c] = 0.0f;
+      hin = lookback_serial<Op>(P, tchunk, b, dc);
     }
-#pragma unroll
-    for (int c = 0; c < V; ++c) s_hin[lane * V + c] = hin[c];
+  }
+  if (chan_on) {
+    s_hin[tid] = hin;
+    if (tchunk + 1 < P.n_tchunks)
+      store_word(P.state + size_t(tchunk) * plane + size_t(b) * P.D + dc,
+                 pack_state(Op::apply(run, hin)));
   }
   __syncthreads();
 
@@ -377,14 +405,17 @@ void chunk_scan_kernel(const ScanParams P) {
   float h[V];
 #pragma unroll
   for (int c = 0; c < V; ++c) h[c] = Op::apply(s_pre[wave][lane * V + c], s_hin[lane * V + c]);
-  float* out = P.out + size_t(b * P.T) * size_t(P.D) + size_t(d);
+  const int64_t out_base = row0 * P.D + dtile_first;
+  const rsrc_t ro = make_rsrc(P.out + out_base, (P.B * P.T * P.D - out_base) * 4);
+  const int voff_out = lane * V * 4;
+  const int out_row_bytes = int(P.D * 4);
 #pragma unroll
   for (int n = 0; n < N; ++n) {
 #pragma unroll
     for (int c = 0; c < V; ++c) h[c] = Op::apply(e[n][c], h[c]);
     const int64_t t = tw + n;
     if (lane_on && t < P.T) {
-      OutVec<V>::store(out + size_t(t) * size_t(P.D), h);
+      OutVec<V>::store(ro, voff_out, n * out_row_bytes, h);
       if (P.last != nullptr && t == P.T - 1) {
 #pragma unroll
         for (int c = 0; c < V; ++c) P.last[size_t(b) * P.D + d + c] = h[c];
@@ -418,11 +449,7 @@ hipError_t launch_v(const ScanParams& P, hipStream_t stream) {
 
 template <class Op, typename TIn>
 hipError_t launch_op(int V, const ScanParams& P, hipStream_t stream) {
-  switch (V) {
-    case 4: return launch_v<Op, TIn, 4>(P, stream);
-    case 2: return launch_v<Op, TIn, 2>(P, stream);
-    default: return launch_v<Op, TIn, 1>(P, stream);
-  }
+  return V == 2 ? launch_v<Op, TIn, 2>(P, stream) : launch_v<Op, TIn, 1>(P, stream);
 }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -430,21 +457,16 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 }  // namespace
 
 ScanGeometry choose_geometry(const ScanRequest& rq) {
+  // Two channels per lane when the data allows it: 128-channel tiles keep
+  // many independent chains along T (so few tiles of a chain are in flight
+  // at once and the look-back window reaches a finished tile), with 4-byte
+  // bf16 / 8-byte fp32 accesses that still cover whole cache lines per wave.
   const size_t esz = rq.in_dtype == SR_BF16 ? 2 : 4;
   int V = 1;
-  for (int cand : {4, 2}) {
-    const bool fits = rq.D % cand == 0 && rq.ld_in % cand == 0 &&
-                      aligned(rq.in0, esz * cand) && aligned(rq.in1, esz * cand) &&
-                      aligned(rq.out, 4 * cand);
-    if (!fits) continue;
-    // Prefer the widest vector that leaves no more idle lanes than V = 1 does.
-    const int64_t tiles_c = (rq.D + 64 * cand - 1) / (64 * cand);
-    const int64_t tiles_1 = (rq.D + 63) / 64;
-    if (tiles_c * 64 * cand <= tiles_1 * 64) {
-      V = cand;
-      break;
-    }
-  }
+  const bool v2 = rq.D % 2 == 0 && rq.ld_in % 2 == 0 && aligned(rq.in0, esz * 2) &&
+                  aligned(rq.in1, esz * 2) && aligned(rq.out, 8);
+  const int64_t tiles_2 = (rq.D + 127) / 128, tiles_1 = (rq.D + 63) / 64;
+  if (v2 && tiles_2 * 128 <= tiles_1 * 64) V = 2;
   ScanGeometry g;
   g.V = V;
   g.N = kElemsPerLane / V;
@@ -457,8 +479,8 @@ ScanGeometry choose_geometry(const ScanRequest& rq) {
 }
 
 size_t scan_workspace_bytes(int64_t B, int64_t T, int64_t D) {
-  // The shortest tile along T (V = 4) needs the most look-back words.
-  const int64_t min_tc = int64_t(kWaves) * (kElemsPerLane / 4);
+  // The shortest tile along T (V = 2) needs the most look-back words.
+  const int64_t min_tc = int64_t(kWaves) * (kElemsPerLane / 2);
   const int64_t n_tchunks = (T + min_tc - 1) / min_tc;
   return kHeaderBytes + align_up(size_t(n_tchunks) * size_t(B) * size_t(D) * 8, kAlign);
 }
