@@ -66,8 +66,9 @@ constexpr uint32_t kTagState = 0xFFFFFFFEu;
 constexpr uint32_t kCanonNaN = 0x7FC00000u;
 constexpr uint32_t kSpinLimit = 1u << 20;
 constexpr size_t kHeaderBytes = 256;
-constexpr int kWaves = 8;            // waves per workgroup
-constexpr int kElemsPerLane = 32;    // N * V: maps each lane keeps in registers
+constexpr int kWaves = 12;           // waves per workgroup
+constexpr int kElemsPerLane = 24;    // N * V: maps each lane keeps in registers
+constexpr int kWavesPerSimd = 6;     // register budget: waves resident per SIMD
 constexpr int kWindowWords = 2048;   // look-back words fetched per round trip (16 KiB)
 
 struct Pair {
@@ -118,6 +119,10 @@ struct MinMaxOp {
 // zero instead of faulting.  Word 3 is the gfx9-family raw-buffer format.
 using rsrc_t = __amdgpu_buffer_rsrc_t;
 constexpr int kRsrcWord3 = 0x00020000;
+// Cache policy of the streaming accesses: non-temporal (each input element is
+// read once and each output written once, so they should not displace
+// anything in L2 / the MALL).
+constexpr int kStreamPolicy = 2;
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
   const int64_t n = bytes <= 0 ? 0 : (bytes > int64_t(0xFFFFFFFF) ? int64_t(0xFFFFFFFF) : bytes);
@@ -133,7 +138,7 @@ template <typename TIn, int V> struct Raw;
 template <> struct Raw<uint16_t, 1> {  // bf16
   using type = uint32_t;
   static __device__ __forceinline__ type load(rsrc_t r, int voff, int soff) {
-    return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+    return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, kStreamPolicy);
   }
   static __device__ __forceinline__ void unpack(type x, float (&f)[1]) {
     f[0] = __uint_as_float(x << 16);
@@ -142,7 +147,7 @@ template <> struct Raw<uint16_t, 1> {  // bf16
 template <> struct Raw<uint16_t, 2> {
   using type = uint32_t;
   static __device__ __forceinline__ type load(rsrc_t r, int voff, int soff) {
-    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kStreamPolicy);
   }
   static __device__ __forceinline__ void unpack(type x, float (&f)[2]) {
     f[0] = __uint_as_float(x << 16);
@@ -152,14 +157,14 @@ template <> struct Raw<uint16_t, 2> {
 template <> struct Raw<float, 1> {
   using type = uint32_t;
   static __device__ __forceinline__ type load(rsrc_t r, int voff, int soff) {
-    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kStreamPolicy);
   }
   static __device__ __forceinline__ void unpack(type x, float (&f)[1]) { f[0] = __uint_as_float(x); }
 };
 template <> struct Raw<float, 2> {
   using type = u32x2;
   static __device__ __forceinline__ type load(rsrc_t r, int voff, int soff) {
-    return __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+    return __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kStreamPolicy);
   }
   static __device__ __forceinline__ void unpack(type x, float (&f)[2]) {
     f[0] = __uint_as_float(x.x);
@@ -170,7 +175,7 @@ template <> struct Raw<float, 2> {
 template <int V> struct OutVec;
 template <> struct OutVec<1> {
   static __device__ __forceinline__ void store(rsrc_t r, int voff, int soff, const float (&h)[1]) {
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(h[0]), r, voff, soff, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(h[0]), r, voff, soff, kStreamPolicy);
   }
 };
 template <> struct OutVec<2> {
@@ -178,7 +183,7 @@ template <> struct OutVec<2> {
     u32x2 v;
     v.x = __float_as_uint(h[0]);
     v.y = __float_as_uint(h[1]);
-    __builtin_amdgcn_raw_buffer_store_b64(v, r, voff, soff, 0);
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, voff, soff, kStreamPolicy);
   }
 };
 
@@ -257,7 +262,7 @@ __device__ float lookback_serial(const ScanParams& P, int64_t tchunk, int64_t b,
 }
 
 template <class Op, typename TIn, int V>
-__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4)))
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd)))
 void chunk_scan_kernel(const ScanParams P) {
   constexpr int N = kElemsPerLane / V;
   constexpr int W = kWaves;

@@ -1,0 +1,163 @@
+"""GPU parity of the full minGRU layer (projections on the matrix cores, the
+scan, the output projection) and of the single-token step, against the fp64
+oracle, through the C ABI."""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import metrics, mingru
+from tests.gpu_util import TOL_F32, dev, host64, say
+
+pytestmark = pytest.mark.gpu
+
+sr = pytest.importorskip("scan_linear_rnn_amd")
+
+
+def _layer_inputs(cfg_id):
+    cfg = synth.CONFIGS[cfg_id]
+    B, T, D = cfg["B"], cfg["T"], cfg["D"]
+    x = synth.normal_bt(cfg_id, "x", B, T, D)
+    W_in = synth.normal_mat(cfg_id, "W_in", D, 2 * D, cfg["w_std"])
+    W_out = synth.normal_mat(cfg_id, "W_out", D, D, cfg["w_std"])
+    return x, W_in, W_out
+
+
+def _check_layer(x, W_in, W_out, h0=None, tol=TOL_F32):
+    y, last = sr.mingru_forward(dev(x), dev(W_in), W_out=None if W_out is None else dev(W_out),
+                                h0=None if h0 is None else dev(h0), return_last=True)
+    y_ref, h_ref, last_ref = mingru.layer(x, W_in, W_out, h0)
+    k, p = mingru.layer_kp(x, W_in)
+    carry, inp = mingru.scan_terms(k, p, h0)
+    if W_out is None:
+        err = metrics.h_rel_err(host64(y), h_ref, carry, inp)
+    else:
+        err = metrics.y_rel_err(host64(y), y_ref, h_ref, W_out)
+    err_last = metrics.h_rel_err(host64(last)[:, None], h_ref[:, -1:], carry[:, -1:], inp[:, -1:])
+    say("layer err", err, "last err", err_last)
+    assert err < tol and err_last < tol, (err, err_last)
+    return y
+
+
+@pytest.mark.parametrize("cfg_id", [1, 2])
+def test_layer_configs_match_oracle(cfg_id):
+    say(f"layer config {cfg_id}")
+    x, W_in, W_out = _layer_inputs(cfg_id)
+    y = _check_layer(x, W_in, W_out)
+    assert tuple(y.shape) == x.shape  # output has the input's shape
+
+
+@pytest.mark.parametrize("B,T,D_in,D_h,D_out,with_out,with_h0", [
+    (3, 77, 50, 37, 29, True, True),      # nothing divides anything
+    (2, 300, 128, 96, 96, False, False),  # no output projection
+    (1, 5, 3, 2, 7, True, False),          # tiny K
+    (2, 130, 260, 130, 64, True, True),    # several M, N, K tiles with tails
+])
+def test_layer_ragged_shapes(B, T, D_in, D_h, D_out, with_out, with_h0):
+    say(f"layer ragged {B} {T} {D_in} {D_h} {D_out}")
+    rng = np.random.default_rng([700, B, T, D_in])
+    x = rng.standard_normal((B, T, D_in)).astype(np.float32)
+    W_in = (rng.standard_normal((D_in, 2 * D_h)) / np.sqrt(D_in)).astype(np.float32)
+    W_out = (rng.standard_normal((D_h, D_out)) / np.sqrt(D_h)).astype(np.float32) if with_out else None
+    h0 = rng.uniform(0, 1, (B, D_h)).astype(np.float32) if with_h0 else None
+    _check_layer(x, W_in, W_out, h0)
+
+
+def test_step_loop_matches_oracle_and_parallel_mode():
+    """Config 2's sequential mode: 1024 token steps from a zero state, each
+    checked against the oracle's step, and the final state against the
+    parallel forward (the pages' parallel-vs-sequential comparison)."""
+    say("step loop config 2")
+    x, W_in, W_out = _layer_inputs(2)
+    B, T, D = x.shape
+    xd, Wi, Wo = dev(x), dev(W_in), dev(W_out)
+    y_par, h_par = sr.mingru_forward(xd, Wi, W_out=Wo, return_last=True)
+    h = None
+    ys = []
+    for t in range(T):
+        y_t, h = sr.mingru_step(xd[:, t].contiguous(), Wi, Wo, h_prev=h)
+        ys.append(y_t)
+    y_seq = torch.stack(ys, dim=1)
+    y_ref, h_all, last_ref = mingru.layer(x, W_in, W_out)
+    err = metrics.y_rel_err(host64(y_seq), y_ref, h_all, W_out)
+    say("step err", err)
+    assert err < TOL_F32
+    # Parallel mode and sequential mode agree with each other.
+    assert float((y_seq - y_par).abs().max()) < 1e-4 * float(y_par.abs().max())
+    assert float((h - h_par).abs().max()) < 1e-5
+
+
+def test_step_in_place_and_without_output_projection():
+    rng = np.random.default_rng(701)
+    B, D_in, D_h = 5, 33, 70
+    W_in = (rng.standard_normal((D_in, 2 * D_h)) / np.sqrt(D_in)).astype(np.float32)
+    xs = rng.standard_normal((6, B, D_in)).astype(np.float32)
+    Wi = dev(W_in)
+    h = torch.zeros((B, D_h), device="cuda")
+    h_ref = np.zeros((B, D_h))
+    for t in range(6):
+        y_t, h2 = sr.mingru_step(dev(xs[t]), Wi, None, h_prev=h, h_next=h)  # in place
+        assert h2.data_ptr() == h.data_ptr() and y_t.data_ptr() == h.data_ptr()
+        _, h_ref = mingru.step(xs[t], W_in, None, h_ref)
+        assert np.max(np.abs(host64(h) - h_ref) / np.abs(h_ref)) < 1e-5
+
+
+def test_layer_object_api():
+    torch.manual_seed(0)
+    layer = sr.MinGRU(64)
+    x = torch.randn(2, 40, 64, device="cuda")
+    y = layer(x)
+    assert y.shape == x.shape
+    # Token by token with the carried state matches the parallel call.
+    prev = None
+    outs = []
+    for x_t in x.unbind(dim=1):
+        y_t, prev = layer(x_t, prev_hidden=prev, return_next_prev_hidden=True)
+        outs.append(y_t)
+    y_seq = torch.stack(outs, dim=1)
+    assert float((y_seq - y).abs().max()) < 1e-4 * float(y.abs().max())
+    # The per-token step returns the new hidden state (the base step of the
+    # tutorial: a (4, 32) token and hidden size 64 give a (4, 64) state).
+    small = sr.MinGRU(32, expansion=2.0, W_out=False)
+    y_t, h_t = small(torch.randn(4, 32, device="cuda"), None, return_next_prev_hidden=True)
+    assert tuple(h_t.shape) == (4, 64) and tuple(y_t.shape) == (4, 64)
+
+
+def test_decode_config_4():
+    """Config 4: B=256 streams, D=2048; a parallel prefill of 512 steps, then
+    4096 single-token steps carrying h.  The final state must match the
+    parallel forward over the concatenated 4608-step sequence; two seeded
+    rows are also checked against the fp64 oracle after steps 1, 2, 8 and at
+    the end (the prefill's carry is still visible in the first steps)."""
+    cfg = synth.CONFIGS[4]
+    B, D, Tp, S = cfg["B"], cfg["D"], cfg["T_prefill"], cfg["steps"]
+    say("decode config 4")
+    W_in = synth.device_normal(4, "W_in", (D, 2 * D), 0.0, cfg["w_std"])
+    W_out = synth.device_normal(4, "W_out", (D, D), 0.0, cfg["w_std"])
+    x = synth.device_normal(4, "x", (B, Tp + S, D))
+    _, h = sr.mingru_forward(x[:, :Tp], W_in, W_out=W_out, return_last=True)
+    rows = [3, 201]
+    snaps = {}
+    for t in range(S):
+        y_t, h = sr.mingru_step(x[:, Tp + t].contiguous(), W_in, W_out, h_prev=h)
+        if t + 1 in (1, 2, 8):
+            snaps[t + 1] = h[rows].double().cpu().numpy()
+    y_full, h_full = sr.mingru_forward(x, W_in, W_out=W_out, return_last=True)
+    rel = float((h - h_full).abs().max() / h_full.abs().max())
+    say("decode vs parallel", rel)
+    assert rel < 1e-4
+    # Oracle on two rows in fp64: the whole 4608-step sequence run
+    # sequentially (the projections of every step are one matmul).
+    xr = x[rows].double().cpu().numpy()
+    Wi = W_in.double().cpu().numpy()
+    _, h_all, _ = mingru.layer(xr, Wi, None)
+    for step, got in snaps.items():
+        ref = h_all[:, Tp + step - 1]
+        e = np.max(np.abs(got - ref) / np.abs(ref))
+        say("decode step", step, "err", e)
+        assert e < TOL_F32
+    ref = h_all[:, -1]
+    e = np.max(np.abs(h[rows].double().cpu().numpy() - ref) / np.abs(ref))
+    say("decode final err", e)
+    assert e < TOL_F32
