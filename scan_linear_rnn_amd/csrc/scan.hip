@@ -69,7 +69,7 @@ constexpr size_t kHeaderBytes = 256;
 constexpr int kWaves = 12;           // waves per workgroup
 constexpr int kElemsPerLane = 24;    // N * V: maps each lane keeps in registers
 constexpr int kWavesPerSimd = 6;     // register budget: waves resident per SIMD
-constexpr int kWindowWords = 2048;   // look-back words fetched per round trip (16 KiB)
+constexpr int kWindowTiles = 4;      // preceding tiles whose look-back words one round trip fetches
 
 struct Pair {
   float u, v;
@@ -248,7 +248,7 @@ __device__ float lookback_serial(const ScanParams& P, int64_t tchunk, int64_t b,
       __hip_atomic_store(P.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       return __uint_as_float(kCanonNaN);
     }
-    __builtin_amdgcn_s_sleep(1);
+    __builtin_amdgcn_s_sleep(8);  // ~512 cycles between polls of an unwritten word
   }
   // Forward: apply the maps of tiles i+1 .. tchunk-1 in order.
   for (int64_t m = i + 1; m < tchunk; ++m) {
@@ -269,7 +269,7 @@ void chunk_scan_kernel(const ScanParams P) {
   using R = Raw<TIn, V>;
   __shared__ uint32_t s_ticket;
   __shared__ Pair s_pre[W][64 * V];
-  __shared__ uint64_t s_win[kWindowWords / (64 * V)][64 * V];
+  __shared__ uint64_t s_win[kWindowTiles][64 * V];
   __shared__ float s_hin[64 * V];
 
   const int lane = threadIdx.x & 63;
@@ -340,7 +340,7 @@ void chunk_scan_kernel(const ScanParams P) {
   // Phase 2: one thread per channel combines the waves' maps and resolves
   // the state entering the tile.
   constexpr int Dc = 64 * V;
-  constexpr int kWin = kWindowWords / Dc;  // predecessor tiles fetched at once
+  constexpr int kWin = kWindowTiles;
   const int tid = threadIdx.x;
   const int64_t dtile0 = int64_t(chain % n_dtiles) * Dc;
   const bool chan_thread = tid < Dc;
