@@ -213,7 +213,7 @@ def mingru_forward(x=None, W_in=None, *, k=None, p=None, h0=None, W_out=None,
     return (y, h_last) if return_last else y
 
 
-def mingru_step(x_t, W_in, W_out=None, h_prev=None, h_next=None):
+def mingru_step(x_t, W_in, W_out=None, h_prev=None, h_next=None, workspace=None):
     """Sequential mode, one token: x_t [B,D_in] -> (y_t [B,D_out], h_t [B,D_h]).
 
     ``h_prev`` None is the zero state.  ``h_next`` may be given (it may be the
@@ -246,8 +246,13 @@ def mingru_step(x_t, W_in, W_out=None, h_prev=None, h_next=None):
     else:
         D_out = D_h
         y_t = None
+    nbytes = _lib.mingru_step_workspace_size(B, D_in, D_h, D_out)
+    ws = None
+    if nbytes:
+        ws = workspace if workspace is not None and workspace.numel() >= nbytes else _workspace(nbytes, device)
     st = _lib.mingru_step(B, D_in, D_h, D_out, _ptr(x_t), _ptr(W_in), _ptr(W_out), _ptr(h_prev),
-                          _ptr(h_next), _ptr(y_t), None, 0, _stream(device))
+                          _ptr(h_next), _ptr(y_t), _ptr(ws), 0 if ws is None else ws.numel(),
+                          _stream(device))
     _check("mingru_step", st)
     return (h_next if y_t is None else y_t), h_next
 

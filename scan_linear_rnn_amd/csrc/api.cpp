@@ -29,18 +29,31 @@ bool aligned(const void* p, size_t a) { return reinterpret_cast<uintptr_t>(p) % 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
 struct FwdLayout {
-  size_t scan_bytes, kp_off, kp_bytes, h_off, h_bytes, total;
+  size_t scan_bytes, kp_off, kp_bytes, h_off, h_bytes, g_off, g_bytes, total;
 };
 
-FwdLayout forward_layout(int64_t B, int64_t T, int64_t D_h, bool w_in, bool w_out) {
+// Workspace of a forward call: the scan's look-back words, the staged [k|p]
+// and h when the projections run, and split-K partial sums of the GEMMs.
+FwdLayout forward_layout(int64_t B, int64_t T, int64_t D_in, int64_t D_h, int64_t D_out,
+                         bool w_in, bool w_out) {
   FwdLayout L{};
   L.scan_bytes = align_up(scan_workspace_bytes(B, T, D_h), kAlign);
   L.kp_off = L.scan_bytes;
   L.kp_bytes = w_in ? align_up(size_t(B) * size_t(T) * size_t(2 * D_h) * 4, kAlign) : 0;
   L.h_off = L.kp_off + L.kp_bytes;
   L.h_bytes = w_out ? align_up(size_t(B) * size_t(T) * size_t(D_h) * 4, kAlign) : 0;
-  L.total = L.h_off + L.h_bytes;
+  L.g_off = L.h_off + L.h_bytes;
+  const size_t g_in = w_in ? gemm_workspace_bytes(B * T, 2 * D_h, D_in, false) : 0;
+  const size_t g_out = w_out ? gemm_workspace_bytes(B * T, D_out, D_h, false) : 0;
+  L.g_bytes = g_in > g_out ? g_in : g_out;
+  L.total = L.g_off + L.g_bytes;
   return L;
+}
+
+size_t step_workspace(int64_t B, int64_t D_in, int64_t D_h, int64_t D_out) {
+  const size_t a = gemm_workspace_bytes(B, 2 * D_h, D_in, true);
+  const size_t b = gemm_workspace_bytes(B, D_out, D_h, false);
+  return a > b ? a : b;
 }
 
 sr_status check_workspace(void* ws, size_t have, size_t need) {
@@ -79,11 +92,9 @@ const char* scanrnn_version(void) { return "0.1.0"; }
 
 size_t mingru_forward_workspace_size(int64_t B, int64_t T, int64_t D_in, int64_t D_h,
                                      int64_t D_out, int has_w_in, int has_w_out) {
-  (void)D_in;
-  (void)D_out;
   int64_t n;
-  if (B < 0 || T < 0 || D_h < 0 || !prod3(B, T, 2 * D_h, &n)) return 0;
-  return forward_layout(B, T, D_h, has_w_in != 0, has_w_out != 0).total;
+  if (B < 0 || T < 0 || D_in < 0 || D_h < 0 || D_out < 0 || !prod3(B, T, 2 * D_h, &n)) return 0;
+  return forward_layout(B, T, D_in, D_h, D_out, has_w_in != 0, has_w_out != 0).total;
 }
 
 sr_status mingru_forward(int64_t B, int64_t T, int64_t D_in, int64_t D_h, int64_t D_out,
@@ -120,7 +131,7 @@ sr_status mingru_forward(int64_t B, int64_t T, int64_t D_in, int64_t D_h, int64_
     int64_t span;
     SR_REQUIRE(prod3(B, T, ld_kp, &span), "k/p extent overflows int64");
   }
-  const FwdLayout L = forward_layout(B, T, D_h, w_in, w_out);
+  const FwdLayout L = forward_layout(B, T, D_in, D_h, D_out, w_in, w_out);
   sr_status st = check_workspace(workspace, workspace_bytes, L.total);
   if (st != SR_OK) return st;
 
@@ -128,6 +139,7 @@ sr_status mingru_forward(int64_t B, int64_t T, int64_t D_in, int64_t D_h, int64_
   char* ws = static_cast<char*>(workspace);
   float* kp_buf = w_in ? reinterpret_cast<float*>(ws + L.kp_off) : nullptr;
   float* h_buf = w_out ? reinterpret_cast<float*>(ws + L.h_off) : y;
+  float* g_buf = L.g_bytes ? reinterpret_cast<float*>(ws + L.g_off) : nullptr;
 
   if (B == 0 || D_h == 0) {
     // No channels: y has no elements unless D_out > 0 with W_out (then y = 0).
@@ -135,7 +147,7 @@ sr_status mingru_forward(int64_t B, int64_t T, int64_t D_in, int64_t D_h, int64_
     return SR_OK;
   }
   if (w_in && T > 0) {
-    st = launch_gemm_f32(B * T, 2 * D_h, D_in, x, D_in, W_in, 2 * D_h, kp_buf, 2 * D_h, s);
+    st = launch_gemm_f32(B * T, 2 * D_h, D_in, x, D_in, W_in, 2 * D_h, kp_buf, 2 * D_h, g_buf, s);
     if (st != SR_OK) return st;
   }
   ScanRequest rq{};
@@ -154,24 +166,22 @@ sr_status mingru_forward(int64_t B, int64_t T, int64_t D_in, int64_t D_h, int64_
   rq.stream = s;
   st = launch_scan(rq);
   if (st != SR_OK) return st;
-  if (w_out && T > 0) st = launch_gemm_f32(B * T, D_out, D_h, h_buf, D_h, W_out, D_out, y, D_out, s);
+  if (w_out && T > 0)
+    st = launch_gemm_f32(B * T, D_out, D_h, h_buf, D_h, W_out, D_out, y, D_out, g_buf, s);
   return st;
 }
 
 size_t mingru_step_workspace_size(int64_t B, int64_t D_in, int64_t D_h, int64_t D_out) {
-  (void)B;
-  (void)D_in;
-  (void)D_h;
-  (void)D_out;
-  return 0;
+  int64_t n;
+  if (B < 0 || D_in < 0 || D_h < 0 || D_out < 0 || !prod3(B, 2 * D_h + D_out, D_in + D_h + 1, &n))
+    return 0;
+  return step_workspace(B, D_in, D_h, D_out);
 }
 
 sr_status mingru_step(int64_t B, int64_t D_in, int64_t D_h, int64_t D_out, const float* x_t,
                       const float* W_in, const float* W_out, const float* h_prev, float* h_next,
                       float* y_t, void* workspace, size_t workspace_bytes, void* stream) {
   g_last_error[0] = '\0';
-  (void)workspace;
-  (void)workspace_bytes;
   SR_REQUIRE(B >= 0 && D_in >= 0 && D_h >= 0 && D_out >= 0,
              "sizes must be non-negative (B=%lld D_in=%lld D_h=%lld D_out=%lld)", (long long)B,
              (long long)D_in, (long long)D_h, (long long)D_out);
@@ -190,11 +200,15 @@ sr_status mingru_step(int64_t B, int64_t D_in, int64_t D_h, int64_t D_out, const
   SR_REQUIRE(aligned(x_t, 4) && aligned(W_in, 4) && aligned(W_out, 4) && aligned(h_prev, 4) &&
                  aligned(h_next, 4) && aligned(y_t, 4),
              "fp32 pointers must be 4-byte aligned");
+  sr_status st = check_workspace(workspace, workspace_bytes, step_workspace(B, D_in, D_h, D_out));
+  if (st != SR_OK) return st;
   if (B == 0) return SR_OK;
   hipStream_t s = as_stream(stream);
-  sr_status st = launch_step_in(B, D_in, D_h, x_t, W_in, h_prev, h_next, s);
+  float* g_buf = static_cast<float*>(workspace);
+  st = launch_step_in(B, D_in, D_h, x_t, W_in, h_prev, h_next, g_buf, s);
   if (st != SR_OK) return st;
-  if (W_out != nullptr) return launch_gemm_f32(B, D_out, D_h, h_next, D_h, W_out, D_out, y_t, D_out, s);
+  if (W_out != nullptr)
+    return launch_gemm_f32(B, D_out, D_h, h_next, D_h, W_out, D_out, y_t, D_out, g_buf, s);
   if (y_t != nullptr && y_t != h_next) return launch_copy_or_zero(y_t, h_next, n_h, s);
   return SR_OK;
 }

@@ -59,17 +59,24 @@ ScanGeometry choose_geometry(const ScanRequest& rq);
 
 // ---------------------------------------------------------------- GEMM
 //
-// C[M,N] = A[M,K] * B[K,N], fp32, row-major with leading dimensions.
+// C[M,N] = A[M,K] * B[K,N], fp32, row-major with leading dimensions.  Small
+// problems split K across workgroups; `ws` must then hold
+// gemm_workspace_bytes(M, N, K, false) bytes (it may be null when that is 0).
 sr_status launch_gemm_f32(int64_t M, int64_t N, int64_t K,
                           const float* A, int64_t lda,
                           const float* Bm, int64_t ldb,
-                          float* C, int64_t ldc, hipStream_t stream);
+                          float* C, int64_t ldc, float* ws, hipStream_t stream);
 
-// Step kernel: h_next = h_prev + z * (g(p) - h_prev) with [k|p] = x_t W_in,
-// computed as one GEMM whose epilogue applies the update.
+// Step kernel: h_next = (1 - z) h_prev + z g(p) with [k|p] = x_t W_in,
+// computed as one GEMM whose epilogue applies the update.  `ws`: as above
+// with gemm_workspace_bytes(Bsz, 2*D_h, D_in, true).
 sr_status launch_step_in(int64_t Bsz, int64_t D_in, int64_t D_h,
                          const float* x_t, const float* W_in,
-                         const float* h_prev, float* h_next, hipStream_t stream);
+                         const float* h_prev, float* h_next, float* ws, hipStream_t stream);
+
+// Number of K slices a GEMM of this shape uses, and the workspace they need.
+int gemm_splits(int64_t M, int64_t N, int64_t K, bool step);
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, bool step);
 
 // Copies n floats (src may be null: writes zeros).
 sr_status launch_copy_or_zero(float* dst, const float* src, int64_t n, hipStream_t stream);
