@@ -239,8 +239,9 @@ def leg_copy(torch):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[1])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    # The GPU reaches steady clocks only after ~0.1 s of sustained work.
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--legs", default="c3,c5,c4,c2,c1,copy")
     ap.add_argument("--cpu-steps", type=int, default=16384,
                     help="sequence prefix the CPU oracle baseline runs over (0 = skip)")

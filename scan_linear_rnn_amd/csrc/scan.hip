@@ -273,11 +273,14 @@ void chunk_scan_kernel(const ScanParams P) {
   __shared__ float s_hin[64 * V];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // The wave index and the ticket are the same in every lane of a wave;
+  // saying so keeps the buffer descriptors built from them in scalar
+  // registers (otherwise each buffer access becomes a uniformity loop).
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (threadIdx.x == 0) s_ticket = atomicAdd(P.counter, 1u);
   __syncthreads();
   // Tickets, chains and tiles all fit in 32 bits (checked on the host).
-  const uint32_t ticket = s_ticket;
+  const uint32_t ticket = __builtin_amdgcn_readfirstlane(s_ticket);
   const uint32_t n_chains = uint32_t(P.n_chains), n_dtiles = uint32_t(P.n_dtiles);
   const uint32_t chain = ticket % n_chains;
   const int64_t tchunk = ticket / n_chains;
