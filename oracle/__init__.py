@@ -17,6 +17,7 @@ Everything here is plain, slow and meant to be checked by eye:
                   parallel form equals the sequential definition.
 * ``minmax``   -- the MinMax neuron's recurrence run sequentially, plus the
                   clamp-composition rule the parallel form relies on.
+* ``grad``     -- the gradients of both scans (backward in time, chain rule).
 * ``metrics``  -- the conditioned error measures used by the parity tests.
 
 Sources: the minGRU-pytorch profile (openvist.com), intro and "Requirements &
@@ -31,4 +32,4 @@ the benchmark spec of the method and are written out here as given.
 Parity status of each function is listed in its module docstring.
 """
 
-from . import logspace, metrics, minmax, mingru, scalar  # noqa: F401
+from . import grad, logspace, metrics, minmax, mingru, scalar  # noqa: F401
