@@ -134,6 +134,44 @@ sr_status minmax_scan(int64_t B, int64_t T, int64_t D,
                       float* x_out, float* x_last,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of workspace the backward calls need. */
+size_t mingru_scan_backward_workspace_size(int64_t B, int64_t T, int64_t D);
+size_t minmax_scan_backward_workspace_size(int64_t B, int64_t T, int64_t D);
+
+/*
+ * Backward pass of the minGRU scan (the layers are trained: minGRU profile,
+ * "Requirements & limits", training entry point).  For L with dL/dh_t = dh
+ * on every output h_t (the scan-only mingru_forward's y) and dL/dh_T =
+ * dh_last, returns
+ *     dk_t = G_t z_t (1 - z_t) (g(p_t) - h_{t-1}),  dp_t = G_t z_t g'(p_t),
+ *     dh0  = (1 - z_1) G_1,   with  G_t = dh_t + (1 - z_{t+1}) G_{t+1}.
+ *
+ *   k, p     the forward inputs (rows of ld_kp elements, kp_dtype).
+ *   h0       [B,D] forward initial state or NULL (zero).
+ *   h        [B,T,D] fp32 forward outputs h_1..h_T.
+ *   dh       [B,T,D] fp32 upstream gradient;  dh_last [B,D] or NULL.
+ *   dk, dp   [B,T,D] fp32 outputs (contiguous).  dh0 [B,D] or NULL.
+ */
+sr_status mingru_scan_backward(int64_t B, int64_t T, int64_t D,
+                               const void* k, const void* p, int64_t ld_kp, sr_dtype kp_dtype,
+                               const float* h0, const float* h, const float* dh,
+                               const float* dh_last, float* dk, float* dp, float* dh0,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward pass of the MinMax scan (minmaxrnc page, "Key properties": the
+ * gradient through the state path neither vanishes nor explodes -- it is
+ * routed, unchanged, to the operand each step selects).  Gradients dx on
+ * x_out and dx_last on x_T; r, s, x0 and x_out are the forward's.  Ties
+ * (measure zero) route to the state: s only if strictly above min(r, x),
+ * r only if strictly below x.  dr, ds [B,T,D], dx0 [B,D] or NULL.
+ */
+sr_status minmax_scan_backward(int64_t B, int64_t T, int64_t D,
+                               const float* r, const float* s, const float* x0,
+                               const float* x_out, const float* dx, const float* dx_last,
+                               float* dr, float* ds, float* dx0,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
 /* Text of the last non-OK status returned on this thread ("" if none). */
 const char* scanrnn_last_error(void);
 

@@ -28,6 +28,8 @@ __all__ = [
     "mingru_forward",
     "mingru_step",
     "minmax_scan",
+    "mingru_scan_backward",
+    "minmax_scan_backward",
     "library_path",
     "ScanRNNError",
 ]
@@ -51,6 +53,10 @@ EXPORTED = (
     "mingru_step",
     "minmax_scan_workspace_size",
     "minmax_scan",
+    "mingru_scan_backward_workspace_size",
+    "mingru_scan_backward",
+    "minmax_scan_backward_workspace_size",
+    "minmax_scan_backward",
     "scanrnn_last_error",
     "scanrnn_workspace_status",
     "scanrnn_version",
@@ -87,6 +93,16 @@ def _load() -> ctypes.CDLL:
     lib.minmax_scan_workspace_size.argtypes = [i64, i64, i64]
     lib.minmax_scan.restype = i32
     lib.minmax_scan.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.mingru_scan_backward_workspace_size.restype = sz
+    lib.mingru_scan_backward_workspace_size.argtypes = [i64, i64, i64]
+    lib.minmax_scan_backward_workspace_size.restype = sz
+    lib.minmax_scan_backward_workspace_size.argtypes = [i64, i64, i64]
+    lib.mingru_scan_backward.restype = i32
+    lib.mingru_scan_backward.argtypes = [i64, i64, i64, vp, vp, i64, i32, vp, vp, vp, vp, vp, vp,
+                                         vp, vp, sz, vp]
+    lib.minmax_scan_backward.restype = i32
+    lib.minmax_scan_backward.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                         sz, vp]
     lib.scanrnn_last_error.restype = ctypes.c_char_p
     lib.scanrnn_last_error.argtypes = []
     lib.scanrnn_workspace_status.restype = i32
@@ -286,6 +302,64 @@ def minmax_scan(r, s, x0, return_last=False, workspace=None, out=None, out_last=
                           ws.numel(), _stream(r.device))
     _check("minmax_scan", st)
     return (out, last) if return_last else out
+
+
+def mingru_scan_backward(k, p, h, dh, h0=None, dh_last=None, workspace=None):
+    """Gradients of the scan-only forward (k, p [, h0]) -> h.
+
+    ``h`` is the forward output, ``dh`` [B,T,D] the gradient on it and
+    ``dh_last`` [B,D] the gradient on the returned final state.  Returns
+    (dk, dp, dh0) in fp32 (dh0 is None when h0 is None)."""
+    if k.dtype not in (torch.float32, torch.bfloat16) or p.dtype != k.dtype:
+        raise TypeError("k and p must both be float32 or both bfloat16")
+    if k.dim() != 3 or p.shape != k.shape:
+        raise ValueError("k and p must be [B,T,D] of the same shape")
+    if k.device.type != "cuda" or p.device != k.device:
+        raise ValueError("k and p must be on the same GPU")
+    B, T, D = k.shape
+    if (k.stride(2) != 1 or p.stride(2) != 1 or k.stride(0) != T * k.stride(1)
+            or p.stride(1) != k.stride(1) or p.stride(0) != k.stride(0)):
+        k = k.contiguous()
+        p = p.contiguous()
+    h = _dev(h, "h", shape=(B, T, D))
+    dh = _dev(dh, "dh", shape=(B, T, D))
+    if h0 is not None:
+        h0 = _dev(h0, "h0", shape=(B, D))
+    if dh_last is not None:
+        dh_last = _dev(dh_last, "dh_last", shape=(B, D))
+    dk = torch.empty((B, T, D), dtype=torch.float32, device=k.device)
+    dp = torch.empty_like(dk)
+    dh0 = torch.empty((B, D), dtype=torch.float32, device=k.device) if h0 is not None else None
+    nbytes = _lib.mingru_scan_backward_workspace_size(B, T, D)
+    ws = workspace if workspace is not None and workspace.numel() >= nbytes else _workspace(nbytes, k.device)
+    st = _lib.mingru_scan_backward(B, T, D, _ptr(k), _ptr(p), k.stride(1),
+                                   SR_BF16 if k.dtype == torch.bfloat16 else SR_F32, _ptr(h0),
+                                   _ptr(h), _ptr(dh), _ptr(dh_last), _ptr(dk), _ptr(dp), _ptr(dh0),
+                                   _ptr(ws), ws.numel(), _stream(k.device))
+    _check("mingru_scan_backward", st)
+    return dk, dp, dh0
+
+
+def minmax_scan_backward(r, s, x0, x_out, dx, dx_last=None, workspace=None):
+    """Gradients of the MinMax scan: returns (dr, ds, dx0) in fp32."""
+    r = _dev(r, "r", ndim=3)
+    B, T, D = r.shape
+    s = _dev(s, "s", shape=(B, T, D))
+    x0 = _dev(x0, "x0", shape=(B, D))
+    x_out = _dev(x_out, "x_out", shape=(B, T, D))
+    dx = _dev(dx, "dx", shape=(B, T, D))
+    if dx_last is not None:
+        dx_last = _dev(dx_last, "dx_last", shape=(B, D))
+    dr = torch.empty_like(r)
+    ds = torch.empty_like(r)
+    dx0 = torch.empty((B, D), dtype=torch.float32, device=r.device)
+    nbytes = _lib.minmax_scan_backward_workspace_size(B, T, D)
+    ws = workspace if workspace is not None and workspace.numel() >= nbytes else _workspace(nbytes, r.device)
+    st = _lib.minmax_scan_backward(B, T, D, _ptr(r), _ptr(s), _ptr(x0), _ptr(x_out), _ptr(dx),
+                                   _ptr(dx_last), _ptr(dr), _ptr(ds), _ptr(dx0), _ptr(ws),
+                                   ws.numel(), _stream(r.device))
+    _check("minmax_scan_backward", st)
+    return dr, ds, dx0
 
 
 def workspace_status(ws: torch.Tensor) -> int:

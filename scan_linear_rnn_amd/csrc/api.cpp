@@ -251,6 +251,80 @@ sr_status minmax_scan(int64_t B, int64_t T, int64_t D, const float* r, const flo
   return launch_scan(rq);
 }
 
+size_t mingru_scan_backward_workspace_size(int64_t B, int64_t T, int64_t D) {
+  int64_t n;
+  if (B < 0 || T < 0 || D < 0 || !prod3(B, T, D, &n)) return 0;
+  return align_up(scan_backward_workspace_bytes(B, T, D), kAlign);
+}
+
+size_t minmax_scan_backward_workspace_size(int64_t B, int64_t T, int64_t D) {
+  return mingru_scan_backward_workspace_size(B, T, D);
+}
+
+sr_status mingru_scan_backward(int64_t B, int64_t T, int64_t D, const void* k, const void* p,
+                               int64_t ld_kp, sr_dtype kp_dtype, const float* h0, const float* h,
+                               const float* dh, const float* dh_last, float* dk, float* dp,
+                               float* dh0, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  g_last_error[0] = '\0';
+  SR_REQUIRE(B >= 0 && T >= 0 && D >= 0, "sizes must be non-negative (B=%lld T=%lld D=%lld)",
+             (long long)B, (long long)T, (long long)D);
+  int64_t n, span;
+  SR_REQUIRE(prod3(B, T, D, &n), "tensor sizes overflow int64");
+  SR_REQUIRE(kp_dtype == SR_F32 || kp_dtype == SR_BF16, "kp_dtype %d unsupported", int(kp_dtype));
+  SR_REQUIRE(ld_kp >= D, "ld_kp (%lld) must be >= D (%lld)", (long long)ld_kp, (long long)D);
+  SR_REQUIRE(prod3(B, T, ld_kp, &span), "k/p extent overflows int64");
+  SR_REQUIRE(n == 0 || (k && p && h && dh && dk && dp), "k, p, h, dh, dk and dp are required");
+  const size_t esz = kp_dtype == SR_BF16 ? 2 : 4;
+  SR_REQUIRE(aligned(k, esz) && aligned(p, esz), "k and p must be aligned to their element size");
+  SR_REQUIRE(aligned(h0, 4) && aligned(h, 4) && aligned(dh, 4) && aligned(dh_last, 4) &&
+                 aligned(dk, 4) && aligned(dp, 4) && aligned(dh0, 4),
+             "fp32 pointers must be 4-byte aligned");
+  sr_status st = check_workspace(workspace, workspace_bytes,
+                                 mingru_scan_backward_workspace_size(B, T, D));
+  if (st != SR_OK) return st;
+  BackwardRequest rq{};
+  rq.op = ScanOp::kMinGRU;
+  rq.in_dtype = kp_dtype;
+  rq.B = B; rq.T = T; rq.D = D;
+  rq.in0 = k; rq.in1 = p; rq.ld_in = ld_kp;
+  rq.fwd = h; rq.fwd0 = h0; rq.grad = dh; rq.grad_last = dh_last;
+  rq.d0 = dk; rq.d1 = dp; rq.dinit = dh0;
+  rq.workspace = workspace;
+  rq.stream = as_stream(stream);
+  return launch_scan_backward(rq);
+}
+
+sr_status minmax_scan_backward(int64_t B, int64_t T, int64_t D, const float* r, const float* s,
+                               const float* x0, const float* x_out, const float* dx,
+                               const float* dx_last, float* dr, float* ds, float* dx0,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error[0] = '\0';
+  SR_REQUIRE(B >= 0 && T >= 0 && D >= 0, "sizes must be non-negative (B=%lld T=%lld D=%lld)",
+             (long long)B, (long long)T, (long long)D);
+  int64_t n, nbd;
+  SR_REQUIRE(prod3(B, T, D, &n) && prod3(B, D, 1, &nbd), "tensor sizes overflow int64");
+  SR_REQUIRE(n == 0 || (r && s && x_out && dx && dr && ds), "r, s, x_out, dx, dr and ds are required");
+  SR_REQUIRE(nbd == 0 || x0 != nullptr, "x0 is required");
+  SR_REQUIRE(aligned(r, 4) && aligned(s, 4) && aligned(x0, 4) && aligned(x_out, 4) &&
+                 aligned(dx, 4) && aligned(dx_last, 4) && aligned(dr, 4) && aligned(ds, 4) &&
+                 aligned(dx0, 4),
+             "fp32 pointers must be 4-byte aligned");
+  sr_status st = check_workspace(workspace, workspace_bytes,
+                                 minmax_scan_backward_workspace_size(B, T, D));
+  if (st != SR_OK) return st;
+  BackwardRequest rq{};
+  rq.op = ScanOp::kMinMax;
+  rq.in_dtype = SR_F32;
+  rq.B = B; rq.T = T; rq.D = D;
+  rq.in0 = r; rq.in1 = s; rq.ld_in = D;
+  rq.fwd = x_out; rq.fwd0 = x0; rq.grad = dx; rq.grad_last = dx_last;
+  rq.d0 = dr; rq.d1 = ds; rq.dinit = dx0;
+  rq.workspace = workspace;
+  rq.stream = as_stream(stream);
+  return launch_scan_backward(rq);
+}
+
 sr_status scanrnn_workspace_status(const void* workspace, void* stream) {
   g_last_error[0] = '\0';
   SR_REQUIRE(workspace != nullptr, "workspace is NULL");

@@ -57,6 +57,28 @@ sr_status launch_scan(const ScanRequest& rq);
 // Chooses the geometry a request will use (exposed for sizing and tests).
 ScanGeometry choose_geometry(const ScanRequest& rq);
 
+// Backward pass of a scan (reverse time, same engine).
+struct BackwardRequest {
+  ScanOp op;
+  sr_dtype in_dtype;    // k,p (minGRU); r,s are fp32
+  int64_t B, T, D;
+  const void* in0;      // k or r
+  const void* in1;      // p or s
+  int64_t ld_in;
+  const float* fwd;     // forward outputs [B,T,D] (h_t or x_{t+1})
+  const float* fwd0;    // forward initial state [B,D] (null = zero; required for MinMax)
+  const float* grad;    // upstream gradient [B,T,D]
+  const float* grad_last;  // gradient on the returned final state [B,D] or null
+  float* d0;            // dk or dr [B,T,D]
+  float* d1;            // dp or ds [B,T,D]
+  float* dinit;         // dh0 or dx0 [B,D] or null
+  void* workspace;
+  hipStream_t stream;
+};
+
+sr_status launch_scan_backward(const BackwardRequest& rq);
+size_t scan_backward_workspace_bytes(int64_t B, int64_t T, int64_t D);
+
 // ---------------------------------------------------------------- GEMM
 //
 // C[M,N] = A[M,K] * B[K,N], fp32, row-major with leading dimensions.  Small

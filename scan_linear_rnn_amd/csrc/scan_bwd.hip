@@ -1,0 +1,313 @@
+// Backward pass of the two scans on the same engine, run in reverse time.
+//
+// The gradient of a linear recurrence is again a linear recurrence, backward
+// in time (the chain rule; the MinMax page's "Key properties" note that
+// gradients through the MinMax state path neither vanish nor explode, and the
+// minGRU profile's "Requirements & limits" name a training entry point).  With
+// dL/dh_t = dh_t given for every output:
+//
+//   minGRU : G_t = a_{t+1} G_{t+1} + dh_t      (a = 1 - z = sigma(-k))
+//            dk_t = G_t z_t a_t (g(p_t) - h_{t-1}),  dp_t = G_t z_t g'(p_t),
+//            dh_0 = a_1 G_1
+//   MinMax : Gamma_{t+1} = c_{t+1} Gamma_{t+2} + dx_{t+1}, c in {0, 1} the
+//            "state passes through" indicator of the step; dr_t / ds_t get
+//            Gamma_{t+1} where r_t / s_t was selected, dx_0 = c_0 Gamma_1.
+//
+// Both are scans of affine maps G -> c G + x, so the forward engine's affine
+// operator, look-back and determinism carry over unchanged.  Scan position u
+// is time t = T-1-u; the step's map is (coefficient of the next step, the
+// step's upstream gradient), with the coefficient of the last time step set
+// to 1 so that the gradient on the returned final state enters as the
+// initial state.  Phase 3 turns each G_t into the step's input gradients from
+// the step's inputs and the forward state before it.
+//
+// Reading for MinMax ties (measure zero for continuous inputs): s is selected
+// only if strictly greater than min(r, x), r only if strictly smaller than x;
+// otherwise the state passes.
+
+#include "scan_engine.hpp"
+
+namespace sr {
+namespace {
+using namespace eng;
+
+constexpr int kBwdWaves = 12;
+constexpr int kBwdElemsPerLane = 8;   // N * V steps kept per lane
+constexpr int kBwdWavesPerSimd = 6;
+
+struct BwdParams {
+  ScanParams core;      // look-back context; core.init = gradient on the final state
+  const void* in0;      // k (minGRU) or r (MinMax)
+  const void* in1;      // p or s
+  int64_t ld_in;
+  const float* fwd;     // forward outputs [B,T,D]: h_t (minGRU), x_{t+1} (MinMax)
+  const float* fwd0;    // forward initial state [B,D] (may be null for minGRU)
+  const float* grad;    // upstream gradient on every output [B,T,D]
+  float* d0;            // dk / dr  [B,T,D]
+  float* d1;            // dp / ds  [B,T,D]
+  float* dinit;         // dh0 / dx0 [B,D] or null
+};
+
+__device__ __forceinline__ void sig_pair(float k, float& z, float& a) {
+  constexpr float kLog2e = 1.4426950408889634f;
+  const float e = __builtin_amdgcn_exp2f(-fabsf(k) * kLog2e);
+  const float big = __builtin_amdgcn_rcpf(1.0f + e);
+  const float small = e * big;
+  z = k >= 0.0f ? big : small;  // sigma(k)
+  a = k >= 0.0f ? small : big;  // 1 - sigma(k)
+}
+
+// g(p) and g'(p).
+__device__ __forceinline__ void g_and_slope(float p, float& g, float& gs) {
+  constexpr float kLog2e = 1.4426950408889634f;
+  const float ep = __builtin_amdgcn_exp2f(fminf(p, 0.0f) * kLog2e);
+  const float sp = ep * __builtin_amdgcn_rcpf(1.0f + ep);  // sigma(p) for p < 0
+  g = p >= 0.0f ? p + 0.5f : sp;
+  gs = p >= 0.0f ? 1.0f : sp * (1.0f - sp);
+}
+
+// MinMax selection at one step: 0 the state passes, 1 r selected, 2 s selected.
+__device__ __forceinline__ int selection(float r, float s, float x) {
+  return s > fminf(r, x) ? 2 : (r < x ? 1 : 0);
+}
+
+enum Kind { kMinGRU = 0, kMinMax = 1 };
+
+// V channels per lane, N steps per lane, W waves.  The wave's rows, at scan
+// step n, are t_n = t_hi - n; loads are clamped into [0, T) and addressed
+// from the lowest row any of them touches, so every buffer offset is
+// non-negative and small.
+template <int KIND, typename TIn, int V, int N, int W>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(kBwdWavesPerSimd)))
+void scan_backward_kernel(const BwdParams Q) {
+  using R = Raw<TIn, V>;
+  using RF = Raw<float, V>;
+  constexpr int Dc = 64 * V;
+  const ScanParams& P = Q.core;
+  __shared__ uint32_t s_ticket;
+  __shared__ Pair s_pre[W][Dc];
+  __shared__ uint64_t s_win[kWindowTiles][Dc];
+  __shared__ float s_hin[Dc];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t ticket = take_ticket(P, &s_ticket);
+  const Tile tl = decode_ticket(P, ticket, Dc);
+  const int64_t d = tl.d0 + lane * V;
+  const bool lane_on = d < P.D;
+  const int64_t T = P.T;
+  const int64_t t_hi = T - 1 - (tl.tchunk * (W * N) + int64_t(wave) * N);
+  const int nvalid = t_hi < 0 ? 0 : (t_hi + 1 >= N ? N : int(t_hi + 1));
+  const int64_t rbase = t_hi - N > 0 ? t_hi - N : 0;
+  auto soff = [&](int64_t row, int64_t row_bytes) -> int {
+    const int64_t r = row < 0 ? 0 : (row > T - 1 ? T - 1 : row);
+    return int((r - rbase) * row_bytes);
+  };
+  const int64_t row0 = tl.b * T + rbase;
+
+  // Descriptors over the inputs, the forward states and the gradients.
+  const int64_t esz = sizeof(TIn);
+  const int64_t in_base = row0 * Q.ld_in + tl.d0;
+  const int64_t in_end = (P.B * T - 1) * Q.ld_in + P.D;
+  const rsrc_t r0 = make_rsrc(static_cast<const TIn*>(Q.in0) + in_base, (in_end - in_base) * esz);
+  const rsrc_t r1 = make_rsrc(static_cast<const TIn*>(Q.in1) + in_base, (in_end - in_base) * esz);
+  const int64_t f_base = row0 * P.D + tl.d0;
+  const int64_t f_end = P.B * T * P.D;
+  const rsrc_t rf = make_rsrc(Q.fwd + f_base, (f_end - f_base) * 4);
+  const rsrc_t rg = make_rsrc(Q.grad + f_base, (f_end - f_base) * 4);
+  const int vin = int(lane * V * esz), vf = lane * V * 4;
+  const int64_t in_row = Q.ld_in * esz, f_row = P.D * 4;
+
+  // Step inputs.  minGRU: in0 rows t_n+1 .. t_n (k), in1 rows t_n (p),
+  // fwd rows t_n - 1 (h_{t-1}).  MinMax: in0/in1 rows t_n+1 .. t_n (r, s),
+  // fwd rows t_n .. t_n - 1 (x_{t+1} .. x_t).
+  typename R::type i0[N + 1], i1[N + 1];
+  typename RF::type fw[N + 1], gr[N];
+#pragma unroll
+  for (int i = 0; i <= N; ++i) {
+    i0[i] = R::load(r0, vin, soff(t_hi + 1 - i, in_row));
+    if (KIND == kMinMax || i < N) i1[i] = R::load(r1, vin, soff(KIND == kMinMax ? t_hi + 1 - i : t_hi - i, in_row));
+    if (KIND == kMinMax || i < N) fw[i] = RF::load(rf, vf, soff(KIND == kMinMax ? t_hi - i : t_hi - 1 - i, f_row));
+    if (i < N) gr[i] = RF::load(rg, vf, soff(t_hi - i, f_row));
+  }
+  // The forward state before step 0 (for t = 0).
+  float init_state[V];
+#pragma unroll
+  for (int c = 0; c < V; ++c)
+    init_state[c] = (lane_on && Q.fwd0 != nullptr) ? Q.fwd0[size_t(tl.b) * P.D + d + c] : 0.0f;
+
+  // Phase 1: the maps G -> coef G + grad of the run's steps, composed.
+  Pair e[N][V];
+  Pair agg[V];
+#pragma unroll
+  for (int c = 0; c < V; ++c) agg[c] = MinGRUOp::identity();
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    const int64_t t = t_hi - n;
+    float gv[V];
+    RF::unpack(gr[n], gv);
+    float coef[V];
+    if (KIND == kMinGRU) {
+      float kn[V];
+      R::unpack(i0[n], kn);  // k_{t+1}
+#pragma unroll
+      for (int c = 0; c < V; ++c) {
+        float z, a;
+        sig_pair(kn[c], z, a);
+        coef[c] = a;
+      }
+    } else {
+      float rn[V], sn[V], xn[V];
+      R::unpack(i0[n], rn);   // r_{t+1}
+      R::unpack(i1[n], sn);   // s_{t+1}
+      RF::unpack(fw[n], xn);  // x_{t+1}
+#pragma unroll
+      for (int c = 0; c < V; ++c) coef[c] = selection(rn[c], sn[c], xn[c]) == 0 ? 1.0f : 0.0f;
+    }
+#pragma unroll
+    for (int c = 0; c < V; ++c) e[n][c] = Pair{t == T - 1 ? 1.0f : coef[c], gv[c]};
+    if (n < nvalid) {
+#pragma unroll
+      for (int c = 0; c < V; ++c) agg[c] = MinGRUOp::compose(agg[c], e[n][c]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (!lane_on) {
+#pragma unroll
+    for (int c = 0; c < V; ++c) agg[c] = MinGRUOp::identity();
+  }
+#pragma unroll
+  for (int c = 0; c < V; ++c) s_pre[wave][lane * V + c] = agg[c];
+  __syncthreads();
+
+  // Phase 2: the gradient entering the tile (decoupled look-back).
+  resolve_tile<MinGRUOp, W, Dc>(P, tl, s_pre, s_win, s_hin);
+
+  // Phase 3: replay to get G at every step and form the input gradients.
+  float G[V];
+#pragma unroll
+  for (int c = 0; c < V; ++c)
+    G[c] = MinGRUOp::apply(s_pre[wave][lane * V + c], s_hin[lane * V + c]);
+  const rsrc_t o0 = make_rsrc(Q.d0 + f_base, (f_end - f_base) * 4);
+  const rsrc_t o1 = make_rsrc(Q.d1 + f_base, (f_end - f_base) * 4);
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    const int64_t t = t_hi - n;
+#pragma unroll
+    for (int c = 0; c < V; ++c) G[c] = MinGRUOp::apply(e[n][c], G[c]);
+    float o0v[V], o1v[V], pass_or_a[V];
+    if (KIND == kMinGRU) {
+      float kt[V], pt[V], hp[V];
+      R::unpack(i0[n + 1], kt);
+      R::unpack(i1[n], pt);
+      RF::unpack(fw[n], hp);
+#pragma unroll
+      for (int c = 0; c < V; ++c) {
+        const float h_prev = t == 0 ? init_state[c] : hp[c];
+        float z, a, g, gs;
+        sig_pair(kt[c], z, a);
+        g_and_slope(pt[c], g, gs);
+        o0v[c] = G[c] * z * a * (g - h_prev);
+        o1v[c] = G[c] * z * gs;
+        pass_or_a[c] = a;
+      }
+    } else {
+      float rt[V], st[V], xt[V];
+      R::unpack(i0[n + 1], rt);
+      R::unpack(i1[n + 1], st);
+      RF::unpack(fw[n + 1], xt);
+#pragma unroll
+      for (int c = 0; c < V; ++c) {
+        const float x_prev = t == 0 ? init_state[c] : xt[c];
+        const int sel = selection(rt[c], st[c], x_prev);
+        o0v[c] = sel == 1 ? G[c] : 0.0f;
+        o1v[c] = sel == 2 ? G[c] : 0.0f;
+        pass_or_a[c] = sel == 0 ? 1.0f : 0.0f;
+      }
+    }
+    if (lane_on && n < nvalid) {
+      OutVec<V>::store(o0, vf, soff(t, f_row), o0v);
+      OutVec<V>::store(o1, vf, soff(t, f_row), o1v);
+      if (t == 0 && Q.dinit != nullptr) {
+#pragma unroll
+        for (int c = 0; c < V; ++c) Q.dinit[size_t(tl.b) * P.D + d + c] = pass_or_a[c] * G[c];
+      }
+    }
+  }
+}
+
+template <int KIND, typename TIn, int V>
+hipError_t launch_bwd_v(const BwdParams& Q, hipStream_t stream) {
+  constexpr int N = kBwdElemsPerLane / V;
+  const int64_t n_blocks = Q.core.n_chains * Q.core.n_tchunks;
+  hipLaunchKernelGGL((scan_backward_kernel<KIND, TIn, V, N, kBwdWaves>), dim3(uint32_t(n_blocks)),
+                     dim3(64 * kBwdWaves), 0, stream, Q);
+  return hipGetLastError();
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+}  // namespace
+
+size_t scan_backward_workspace_bytes(int64_t B, int64_t T, int64_t D) {
+  const int64_t min_tc = int64_t(kBwdWaves) * (kBwdElemsPerLane / 2);
+  const int64_t n_tchunks = (T + min_tc - 1) / min_tc;
+  return kHeaderBytes + align_up(size_t(n_tchunks) * size_t(B) * size_t(D) * 8, kAlign);
+}
+
+sr_status launch_scan_backward(const BackwardRequest& rq) {
+  if (rq.B == 0 || rq.D == 0) return SR_OK;
+  if (rq.T == 0) {
+    // Nothing to scan: the gradient on the initial state is the one on the
+    // returned final state (which then is the initial state itself).
+    if (rq.dinit != nullptr) return launch_copy_or_zero(rq.dinit, rq.grad_last, rq.B * rq.D, rq.stream);
+    return SR_OK;
+  }
+  const size_t esz = rq.in_dtype == SR_BF16 ? 2 : 4;
+  const bool v2 = rq.D % 2 == 0 && rq.ld_in % 2 == 0 && aligned(rq.in0, 2 * esz) &&
+                  aligned(rq.in1, 2 * esz) && aligned(rq.fwd, 8) && aligned(rq.grad, 8) &&
+                  aligned(rq.d0, 8) && aligned(rq.d1, 8) &&
+                  (rq.D + 127) / 128 * 128 <= (rq.D + 63) / 64 * 64;
+  const int V = v2 ? 2 : 1;
+  const int64_t Dc = 64 * V, Tc = int64_t(kBwdWaves) * (kBwdElemsPerLane / V);
+  BwdParams Q{};
+  ScanParams& P = Q.core;
+  P.init = rq.grad_last;
+  P.B = rq.B;
+  P.T = rq.T;
+  P.D = rq.D;
+  P.n_dtiles = (rq.D + Dc - 1) / Dc;
+  P.n_tchunks = (rq.T + Tc - 1) / Tc;
+  P.n_chains = rq.B * P.n_dtiles;
+  if (P.n_chains * P.n_tchunks * (64 * kBwdWaves) > int64_t(0xFFFFFFFFu))
+    return fail(SR_ERR_UNSUPPORTED, "backward scan of %lld tiles exceeds one launch's grid",
+                (long long)(P.n_chains * P.n_tchunks));
+  char* ws = static_cast<char*>(rq.workspace);
+  P.counter = reinterpret_cast<uint32_t*>(ws);
+  P.status = reinterpret_cast<uint32_t*>(ws) + 1;
+  P.state = reinterpret_cast<uint64_t*>(ws + kHeaderBytes);
+  Q.in0 = rq.in0;
+  Q.in1 = rq.in1;
+  Q.ld_in = rq.ld_in;
+  Q.fwd = rq.fwd;
+  Q.fwd0 = rq.fwd0;
+  Q.grad = rq.grad;
+  Q.d0 = rq.d0;
+  Q.d1 = rq.d1;
+  Q.dinit = rq.dinit;
+  sr_status st = reset_workspace(ws, kHeaderBytes + size_t(P.n_tchunks) * size_t(P.B) * size_t(P.D) * 8,
+                                 rq.stream);
+  if (st != SR_OK) return st;
+  hipError_t err;
+  if (rq.op == ScanOp::kMinMax)
+    err = V == 2 ? launch_bwd_v<kMinMax, float, 2>(Q, rq.stream) : launch_bwd_v<kMinMax, float, 1>(Q, rq.stream);
+  else if (rq.in_dtype == SR_BF16)
+    err = V == 2 ? launch_bwd_v<kMinGRU, uint16_t, 2>(Q, rq.stream)
+                 : launch_bwd_v<kMinGRU, uint16_t, 1>(Q, rq.stream);
+  else
+    err = V == 2 ? launch_bwd_v<kMinGRU, float, 2>(Q, rq.stream) : launch_bwd_v<kMinGRU, float, 1>(Q, rq.stream);
+  if (err != hipSuccess) return fail(SR_ERR_HIP, "backward scan launch: %s", hipGetErrorString(err));
+  return SR_OK;
+}
+
+}  // namespace sr

@@ -1,0 +1,188 @@
+"""GPU parity of the scans' backward pass against the fp64 oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import grad, scalar
+from tests.gpu_util import dev, host64, say
+
+pytestmark = pytest.mark.gpu
+
+sr = pytest.importorskip("scan_linear_rnn_amd")
+
+TOL = 1e-4
+
+
+def _abs_G(k, dh, dh_last):
+    """|G|-bound: the reverse recurrence run on |dh| (every term non-negative)."""
+    a = 1.0 - scalar.sigmoid(k)
+    B, T, D = k.shape
+    G = np.zeros((B, D)) if dh_last is None else np.abs(dh_last)
+    out = np.empty((B, T, D))
+    for t in range(T - 1, -1, -1):
+        G = np.abs(dh[:, t]) + G
+        out[:, t] = G
+        G = a[:, t] * G
+    return out
+
+
+def _mingru_errors(k, p, h0, dh, dl, dk, dp, dh0):
+    """Conditioned errors: |d - d_ref| / (|G| z (1-z) (|g| + |h_prev|)) for dk and
+    |d - d_ref| / (|G| z |g'|) for dp, with |G| from _abs_G."""
+    k = np.asarray(k, np.float64)
+    p = np.asarray(p, np.float64)
+    rdk, rdp, rdh0 = grad.mingru_scan_backward(k, p, h0, dh, dl)
+    Gabs = _abs_G(k, dh, dl)
+    z = scalar.sigmoid(k)
+    a = 1.0 - z
+    g = scalar.g(p)
+    B, T, D = k.shape
+    h = np.zeros((B, D)) if h0 is None else np.asarray(h0, np.float64).copy()
+    hp = np.empty_like(k)
+    for t in range(T):
+        hp[:, t] = h
+        h = a[:, t] * h + z[:, t] * g[:, t]
+    den_k = Gabs * z * a * (np.abs(g) + np.abs(hp)) + 1e-30
+    den_p = Gabs * z * grad.g_prime(p) + 1e-30
+    e_k = float(np.max(np.abs(host64(dk) - rdk) / den_k))
+    e_p = float(np.max(np.abs(host64(dp) - rdp) / den_p))
+    e_0 = 0.0
+    if dh0 is not None:
+        e_0 = float(np.max(np.abs(host64(dh0) - rdh0) / (a[:, 0] * Gabs[:, 0] + 1e-30)))
+    return e_k, e_p, e_0
+
+
+@pytest.mark.parametrize("B,T,D,with_h0,with_last", [
+    (2, 64, 16, False, False),
+    (3, 1000, 200, True, True),
+    (2, 4096, 512, True, False),
+    (1, 1, 8, True, True),
+    (2, 3, 3, False, True),
+    (1, 777, 130, True, True),
+])
+def test_mingru_backward_f32(B, T, D, with_h0, with_last):
+    say(f"mingru bwd f32 B={B} T={T} D={D}")
+    rng = np.random.default_rng([1100, B, T, D])
+    k = rng.normal(-1.0, 1.5, (B, T, D)).astype(np.float32)
+    p = rng.standard_normal((B, T, D)).astype(np.float32)
+    h0 = rng.standard_normal((B, D)).astype(np.float32) if with_h0 else None
+    dh = rng.standard_normal((B, T, D)).astype(np.float32)
+    dl = rng.standard_normal((B, D)).astype(np.float32) if with_last else None
+    kd, pd = dev(k), dev(p)
+    h0d = None if h0 is None else dev(h0)
+    h = sr.mingru_forward(k=kd, p=pd, h0=h0d)
+    dk, dp, dh0 = sr.mingru_scan_backward(kd, pd, h, dev(dh), h0=h0d,
+                                          dh_last=None if dl is None else dev(dl))
+    errs = _mingru_errors(k, p, h0, dh, dl, dk, dp, dh0)
+    say("errors", errs)
+    assert max(errs) < TOL, errs
+
+
+def test_mingru_backward_bf16_reduced_c3():
+    B, T, D = 2, 4096, 1024
+    say("mingru bwd bf16")
+    cfg = synth.CONFIGS[3]
+    k32 = synth.normal_bt(3, "k", B, T, D, cfg["k_mean"], cfg["k_std"])
+    p32 = synth.normal_bt(3, "p", B, T, D, cfg["p_mean"], cfg["p_std"])
+    kb, pb = synth.bf16_round(k32).cuda(), synth.bf16_round(p32).cuda()
+    h0 = synth.normal_vec(3, "h0", B, D)
+    rng = np.random.default_rng(1101)
+    dh = rng.standard_normal((B, T, D)).astype(np.float32)
+    dl = rng.standard_normal((B, D)).astype(np.float32)
+    h = sr.mingru_forward(k=kb, p=pb, h0=dev(h0))
+    dk, dp, dh0 = sr.mingru_scan_backward(kb, pb, h, dev(dh), h0=dev(h0), dh_last=dev(dl))
+    errs = _mingru_errors(kb.double().cpu().numpy(), pb.double().cpu().numpy(), h0, dh, dl,
+                          dk, dp, dh0)
+    say("errors", errs)
+    assert max(errs) < 1e-4, errs
+
+
+def test_mingru_backward_repeatable():
+    B, T, D = 2, 5000, 256
+    rng = np.random.default_rng(1102)
+    kd = dev(rng.normal(-2.0, 1.0, (B, T, D)).astype(np.float32))
+    pd = dev(rng.standard_normal((B, T, D)).astype(np.float32))
+    dh = dev(rng.standard_normal((B, T, D)).astype(np.float32))
+    h = sr.mingru_forward(k=kd, p=pd)
+    ref = sr.mingru_scan_backward(kd, pd, h, dh)
+    for _ in range(2):
+        again = sr.mingru_scan_backward(kd, pd, h, dh)
+        assert torch.equal(again[0], ref[0]) and torch.equal(again[1], ref[1])
+
+
+def _minmax_case(B, T, D, seed):
+    rng = np.random.default_rng([1110, seed])
+    r = rng.uniform(-1, 1, (B, T, D)).astype(np.float32)
+    s = (rng.uniform(-1, 1, (B, T, D)) - 0.5).astype(np.float32)
+    x0 = rng.uniform(-1, 1, (B, D)).astype(np.float32)
+    for a in (r, s, x0):
+        a[a == 0] = 0.0
+    dx = rng.standard_normal((B, T, D)).astype(np.float32)
+    dl = rng.standard_normal((B, D)).astype(np.float32)
+    return r, s, x0, dx, dl
+
+
+@pytest.mark.parametrize("B,T,D", [(2, 64, 16), (3, 1000, 200), (1, 1, 5), (2, 5000, 192),
+                                   (4, 333, 7)])
+def test_minmax_backward(B, T, D):
+    say(f"minmax bwd B={B} T={T} D={D}")
+    r, s, x0, dx, dl = _minmax_case(B, T, D, seed=B + T + D)
+    rd, sd, x0d = dev(r), dev(s), dev(x0)
+    x_out = sr.minmax_scan(rd, sd, x0d)
+    dr, ds, dx0 = sr.minmax_scan_backward(rd, sd, x0d, x_out, dev(dx), dx_last=dev(dl))
+    rdr, rds, rdx0 = grad.minmax_scan_backward(r, s, x0, dx, dl)
+    # The routing (which operand each step selects) is decided exactly.
+    assert np.array_equal(host64(dr) != 0, rdr != 0)
+    assert np.array_equal(host64(ds) != 0, rds != 0)
+    # The routed values are sums of upstream gradients: fp32 sums.
+    scale = np.abs(dx).sum(axis=1).max() + np.abs(dl).max()
+    for got, ref in ((dr, rdr), (ds, rds), (dx0, rdx0)):
+        assert float(np.max(np.abs(host64(got) - ref))) < 1e-5 * scale
+
+
+def test_minmax_backward_hold_and_reset():
+    B, T, D = 2, 20000, 192
+    rng = np.random.default_rng(1120)
+    r = np.full((B, T, D), 2.0, np.float32)
+    s = np.full((B, T, D), -2.0, np.float32)
+    x0 = rng.uniform(-1, 1, (B, D)).astype(np.float32)
+    tstar = 12345
+    r[:, tstar] = -3.0
+    s[:, tstar] = 0.5
+    dx = np.ones((B, T, D), np.float32)  # sums of ones are exact in fp32
+    rd, sd, x0d = dev(r), dev(s), dev(x0)
+    x_out = sr.minmax_scan(rd, sd, x0d)
+    dr, ds, dx0 = sr.minmax_scan_backward(rd, sd, x0d, x_out, dev(dx))
+    assert torch.count_nonzero(dr) == 0
+    assert torch.all(dx0 == float(tstar))
+    assert torch.all(ds[:, tstar] == float(T - tstar))
+    assert torch.count_nonzero(ds) == B * D
+
+
+def test_full_c3_size_backward_sampled():
+    cfg = synth.CONFIGS[3]
+    B, T, D = cfg["B"], cfg["T"], cfg["D"]
+    say("full C3 backward")
+    kb = synth.device_normal(3, "k", (B, T, D), cfg["k_mean"], cfg["k_std"], torch.bfloat16)
+    pb = synth.device_normal(3, "p", (B, T, D), cfg["p_mean"], cfg["p_std"], torch.bfloat16)
+    h0 = synth.device_normal(3, "h0", (B, D))
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1130)
+    dh = torch.empty((B, T, D), device="cuda").normal_(0.0, 1.0, generator=g)
+    h = sr.mingru_forward(k=kb, p=pb, h0=h0)
+    ws = torch.empty(sr.raw_library().mingru_scan_backward_workspace_size(B, T, D),
+                     dtype=torch.uint8, device="cuda")
+    dk, dp, dh0 = sr.mingru_scan_backward(kb, pb, h, dh, h0=h0, workspace=ws)
+    assert sr.workspace_status(ws) == 0
+    assert bool(torch.isfinite(dk).all()) and bool(torch.isfinite(dp).all())
+    rng = np.random.default_rng(1131)
+    bs = torch.as_tensor(rng.integers(0, B, 12), device="cuda")
+    ds_ = torch.as_tensor(rng.integers(0, D, 12), device="cuda")
+    pick = lambda x: x[bs, :, ds_].double().cpu().numpy()[None].transpose(0, 2, 1)
+    errs = _mingru_errors(pick(kb), pick(pb), h0[bs, ds_].double().cpu().numpy()[None],
+                          pick(dh), None, dk[bs, :, ds_][None].transpose(1, 2),
+                          dp[bs, :, ds_][None].transpose(1, 2), dh0[bs, ds_][None])
+    say("full C3 backward errors", errs)
+    assert max(errs) < 1e-4, errs
