@@ -166,6 +166,53 @@ def leg_c5(torch, sr, synth, steps, warmup):
                 frac_of_hbm_peak=alg / (mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS)
 
 
+def leg_c3_backward(torch, sr, synth, steps, warmup):
+    """Backward of the headline scan: reads k, p (bf16), h, dh (fp32), writes
+    dk, dp (fp32): 20 algorithmic bytes per element."""
+    cfg = synth.CONFIGS[3]
+    B, T, D = cfg["B"], cfg["T"], cfg["D"]
+    log(f"[bench] c3 backward B={B} T={T} D={D}")
+    kb = synth.device_normal(3, "k", (B, T, D), cfg["k_mean"], cfg["k_std"], torch.bfloat16)
+    pb = synth.device_normal(3, "p", (B, T, D), cfg["p_mean"], cfg["p_std"], torch.bfloat16)
+    h0 = synth.device_normal(3, "h0", (B, D))
+    h = sr.mingru_forward(k=kb, p=pb, h0=h0)
+    dh = torch.empty_like(h).normal_(0.0, 1.0)
+    ws = torch.empty(sr.raw_library().mingru_scan_backward_workspace_size(B, T, D),
+                     dtype=torch.uint8, device="cuda")
+    wall, mean_ms, min_ms = time_launches(
+        torch, lambda: sr.mingru_scan_backward(kb, pb, h, dh, h0=h0, workspace=ws), steps, warmup)
+    n = B * T * D
+    alg = n * 20 + 3 * B * D * 4
+    res = dict(B=B, T=T, D=D, launch_ms_mean=mean_ms, elements_per_s=n / (wall / steps),
+               achieved_GBps=alg / (mean_ms * 1e-3) / 1e9,
+               frac_of_hbm_peak=alg / (mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS)
+    del kb, pb, h, dh, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def leg_c5_backward(torch, sr, synth, steps, warmup):
+    """Backward of the MinMax scan: reads r, s, x_out, dx, writes dr, ds
+    (fp32): 24 algorithmic bytes per element."""
+    cfg = synth.CONFIGS[5]
+    B, T, D = cfg["B"], cfg["T"], cfg["D"]
+    log(f"[bench] c5 backward B={B} T={T} D={D}")
+    r = synth.device_uniform(5, "r", (B, T, D), -1.0, 1.0)
+    s = synth.device_uniform(5, "s", (B, T, D), -1.5, 0.5)
+    x0 = synth.device_uniform(5, "x0", (B, D), -1.0, 1.0)
+    x_out = sr.minmax_scan(r, s, x0)
+    dx = torch.empty_like(r).normal_(0.0, 1.0)
+    ws = torch.empty(sr.raw_library().minmax_scan_backward_workspace_size(B, T, D),
+                     dtype=torch.uint8, device="cuda")
+    wall, mean_ms, _ = time_launches(
+        torch, lambda: sr.minmax_scan_backward(r, s, x0, x_out, dx, workspace=ws), steps, warmup)
+    n = B * T * D
+    alg = n * 24 + 2 * B * D * 4
+    return dict(B=B, T=T, D=D, launch_ms_mean=mean_ms, elements_per_s=n / (wall / steps),
+                achieved_GBps=alg / (mean_ms * 1e-3) / 1e9,
+                frac_of_hbm_peak=alg / (mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS)
+
+
 def leg_c4(torch, sr, synth, n_steps):
     cfg = synth.CONFIGS[4]
     B, D, Tp = cfg["B"], cfg["D"], cfg["T_prefill"]
@@ -239,10 +286,11 @@ def leg_copy(torch):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[1])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    # The GPU reaches steady clocks only after ~0.1 s of sustained work.
-    ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--legs", default="c3,c5,c4,c2,c1,copy")
+    ap.add_argument("--steps", type=int, default=100)
+    # A fresh process reaches steady clocks only after a few hundred ms of
+    # sustained load (measured: the first ~100 launches run 3-5% slower).
+    ap.add_argument("--warmup", type=int, default=1000)
+    ap.add_argument("--legs", default="c3,c5,c3bwd,c5bwd,c4,c2,c1,copy")
     ap.add_argument("--cpu-steps", type=int, default=16384,
                     help="sequence prefix the CPU oracle baseline runs over (0 = skip)")
     ap.add_argument("--c4-steps", type=int, default=4096)
@@ -270,6 +318,11 @@ def main():
         extra["copy_ceiling"] = leg_copy(torch)
     if "c5" in legs:
         extra["minmax_b8_t32768_d192"] = leg_c5(torch, sr, synth, args.steps, args.warmup)
+    if "c3bwd" in legs:
+        extra["backward_b8_t65536_d1024"] = leg_c3_backward(torch, sr, synth, args.steps, args.warmup)
+    if "c5bwd" in legs:
+        extra["minmax_backward_b8_t32768_d192"] = leg_c5_backward(torch, sr, synth, args.steps,
+                                                                  args.warmup)
     if "c2" in legs:
         extra["layer_b2_t1024_d512"] = leg_layer(torch, sr, synth, 2, 10)
     if "c1" in legs:
