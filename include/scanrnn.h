@@ -134,6 +134,16 @@ sr_status minmax_scan(int64_t B, int64_t T, int64_t D,
                       float* x_out, float* x_last,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * One MinMax step for a single token, O(1) work and O(D) memory per token
+ * (minmaxrnc page, "Key properties": efficient inference as a true RNN;
+ * "Quick start": generation steps one token at a time carrying the state):
+ *     x_next = max(min(r_t, x_prev), s_t)   element-wise over [B, D].
+ * x_next may be the same buffer as x_prev.  No workspace.  Bit-exact.
+ */
+sr_status minmax_step(int64_t B, int64_t D, const float* r_t, const float* s_t,
+                      const float* x_prev, float* x_next, void* stream);
+
 /* Bytes of workspace the backward calls need. */
 size_t mingru_scan_backward_workspace_size(int64_t B, int64_t T, int64_t D);
 size_t minmax_scan_backward_workspace_size(int64_t B, int64_t T, int64_t D);

@@ -53,6 +53,7 @@ EXPORTED = (
     "mingru_step",
     "minmax_scan_workspace_size",
     "minmax_scan",
+    "minmax_step",
     "mingru_scan_backward_workspace_size",
     "mingru_scan_backward",
     "minmax_scan_backward_workspace_size",
@@ -77,7 +78,7 @@ def _load() -> ctypes.CDLL:
     if not os.path.exists(_LIB_PATH):
         raise ImportError(
             f"{_LIB_PATH} is missing: build the HIP library first "
-            "(python -m scan_linear_rnn_amd.build)")
+            "(python scan_linear_rnn_amd/build.py)")
     lib = ctypes.CDLL(_LIB_PATH)
     i64, sz, vp, i32 = ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int
     lib.mingru_forward_workspace_size.restype = sz
@@ -93,6 +94,8 @@ def _load() -> ctypes.CDLL:
     lib.minmax_scan_workspace_size.argtypes = [i64, i64, i64]
     lib.minmax_scan.restype = i32
     lib.minmax_scan.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.minmax_step.restype = i32
+    lib.minmax_step.argtypes = [i64, i64, vp, vp, vp, vp, vp]
     lib.mingru_scan_backward_workspace_size.restype = sz
     lib.mingru_scan_backward_workspace_size.argtypes = [i64, i64, i64]
     lib.minmax_scan_backward_workspace_size.restype = sz
@@ -302,6 +305,27 @@ def minmax_scan(r, s, x0, return_last=False, workspace=None, out=None, out_last=
                           ws.numel(), _stream(r.device))
     _check("minmax_scan", st)
     return (out, last) if return_last else out
+
+
+def minmax_step(r_t, s_t, x_prev, x_next=None):
+    """One MinMax token: x_next = max(min(r_t, x_prev), s_t) over [B, D].
+    ``x_next`` may be ``x_prev`` (in place)."""
+    x_prev = _dev(x_prev, "x_prev", ndim=2)
+    if not x_prev.is_contiguous():
+        raise ValueError("x_prev must be contiguous")
+    B, D = x_prev.shape
+    r_t = _dev(r_t, "r_t", shape=(B, D))
+    s_t = _dev(s_t, "s_t", shape=(B, D))
+    if x_next is None:
+        x_next = torch.empty_like(x_prev)
+    elif not x_next.is_contiguous():
+        raise ValueError("x_next must be contiguous")
+    else:
+        _dev(x_next, "x_next", shape=(B, D))
+    st = _lib.minmax_step(B, D, _ptr(r_t), _ptr(s_t), _ptr(x_prev), _ptr(x_next),
+                          _stream(x_prev.device))
+    _check("minmax_step", st)
+    return x_next
 
 
 def mingru_scan_backward(k, p, h, dh, h0=None, dh_last=None, workspace=None):

@@ -1,6 +1,8 @@
 """Builds libscanrnn.so (HIP, gfx950) in the package directory.
 
-    python -m scan_linear_rnn_amd.build        # or __graft_entry__.build()
+    python scan_linear_rnn_amd/build.py        # or __graft_entry__.build()
+
+(Run it as a script: importing the package would load the library it builds.)
 
 Every HIP source is compiled for gfx950 only, with packed-FP32 instruction
 generation switched off (-packed-fp32-ops), and linked into one shared

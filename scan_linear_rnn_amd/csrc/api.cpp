@@ -251,6 +251,19 @@ sr_status minmax_scan(int64_t B, int64_t T, int64_t D, const float* r, const flo
   return launch_scan(rq);
 }
 
+sr_status minmax_step(int64_t B, int64_t D, const float* r_t, const float* s_t,
+                      const float* x_prev, float* x_next, void* stream) {
+  g_last_error[0] = '\0';
+  SR_REQUIRE(B >= 0 && D >= 0, "sizes must be non-negative (B=%lld D=%lld)", (long long)B,
+             (long long)D);
+  int64_t n;
+  SR_REQUIRE(prod3(B, D, 1, &n), "tensor sizes overflow int64");
+  SR_REQUIRE(n == 0 || (r_t && s_t && x_prev && x_next), "r_t, s_t, x_prev and x_next are required");
+  SR_REQUIRE(aligned(r_t, 4) && aligned(s_t, 4) && aligned(x_prev, 4) && aligned(x_next, 4),
+             "fp32 pointers must be 4-byte aligned");
+  return launch_minmax_step(r_t, s_t, x_prev, x_next, n, as_stream(stream));
+}
+
 size_t mingru_scan_backward_workspace_size(int64_t B, int64_t T, int64_t D) {
   int64_t n;
   if (B < 0 || T < 0 || D < 0 || !prod3(B, T, D, &n)) return 0;

@@ -100,6 +100,10 @@ sr_status launch_step_in(int64_t Bsz, int64_t D_in, int64_t D_h,
 int gemm_splits(int64_t M, int64_t N, int64_t K, bool step);
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, bool step);
 
+// One MinMax step over n channels (x_next may alias x_prev).
+sr_status launch_minmax_step(const float* r, const float* s, const float* x_prev, float* x_next,
+                             int64_t n, hipStream_t stream);
+
 // Copies n floats (src may be null: writes zeros).
 sr_status launch_copy_or_zero(float* dst, const float* src, int64_t n, hipStream_t stream);
 

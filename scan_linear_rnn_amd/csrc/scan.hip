@@ -185,6 +185,14 @@ void chunk_scan_kernel(const ScanParams P) {
   }
 }
 
+// One MinMax step for every channel: x_next = max(min(r, x_prev), s).
+__global__ void minmax_step_kernel(const float* r, const float* s, const float* x_prev,
+                                   float* x_next, int64_t n) {
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride)
+    x_next[i] = MinMaxOp::apply(Pair{r[i], s[i]}, x_prev[i]);
+}
+
 __global__ void copy_or_zero_kernel(float* dst, const float* src, int64_t n) {
   const int64_t stride = int64_t(gridDim.x) * blockDim.x;
   for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride)
@@ -243,6 +251,17 @@ sr_status launch_copy_or_zero(float* dst, const float* src, int64_t n, hipStream
   hipLaunchKernelGGL(copy_or_zero_kernel, dim3(uint32_t(blocks)), dim3(256), 0, stream, dst, src, n);
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return fail(SR_ERR_HIP, "copy kernel launch: %s", hipGetErrorString(err));
+  return SR_OK;
+}
+
+sr_status launch_minmax_step(const float* r, const float* s, const float* x_prev, float* x_next,
+                             int64_t n, hipStream_t stream) {
+  if (n <= 0) return SR_OK;
+  const int64_t blocks = (n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096;
+  hipLaunchKernelGGL(minmax_step_kernel, dim3(uint32_t(blocks)), dim3(256), 0, stream, r, s, x_prev,
+                     x_next, n);
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return fail(SR_ERR_HIP, "MinMax step launch: %s", hipGetErrorString(err));
   return SR_OK;
 }
 

@@ -84,3 +84,17 @@ def test_minmax_empty_sequence():
     e = torch.zeros((1, 0, 2), device="cuda")
     out, last = sr.minmax_scan(e, e, x0, return_last=True)
     assert out.shape == (1, 0, 2) and torch.equal(last, x0)
+
+
+def test_minmax_step_matches_scan_bitwise():
+    """Token-by-token steps (streaming, one token per call) reproduce the
+    parallel scan bit for bit, in place."""
+    B, T, D = 3, 200, 192
+    r, s, x0 = _inputs(B, T, D, seed=650)
+    rd, sd = dev(r), dev(s)
+    full = sr.minmax_scan(rd, sd, dev(x0))
+    x = dev(x0).clone()
+    for t in range(T):
+        y = sr.minmax_step(rd[:, t].contiguous(), sd[:, t].contiguous(), x, x_next=x)
+        assert y.data_ptr() == x.data_ptr()
+        assert torch.equal(x, full[:, t])
