@@ -31,9 +31,9 @@ namespace sr {
 namespace {
 using namespace eng;
 
-constexpr int kBwdWaves = 12;
-constexpr int kBwdElemsPerLane = 8;   // N * V steps kept per lane
-constexpr int kBwdWavesPerSimd = 6;
+constexpr int kBwdWaves = 8;
+constexpr int kBwdElemsPerLane = 16;  // N * V steps kept per lane
+constexpr int kBwdWavesPerSimd = 4;
 
 struct BwdParams {
   ScanParams core;      // look-back context; core.init = gradient on the final state
