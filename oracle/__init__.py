@@ -17,13 +17,17 @@ Everything here is plain, slow and meant to be checked by eye:
                   parallel form equals the sequential definition.
 * ``minmax``   -- the MinMax neuron's recurrence run sequentially, plus the
                   clamp-composition rule the parallel form relies on.
+* ``decay``    -- the minGRU recurrence with per-token time decay of the
+                  carried state (gap-driven, clamped), sequentially.
 * ``grad``     -- the gradients of both scans (backward in time, chain rule).
 * ``metrics``  -- the conditioned error measures used by the parity tests.
 
 Sources: the minGRU-pytorch profile (openvist.com), intro and "Requirements &
 limits" (log-space numerically stable version; parallel and sequential modes
 with a carried hidden state); the minmaxrnc PyPI page, "The model" item 3 (the
-MinMax update) and "Key properties" (bounded operator, prefix-scan depth).
+MinMax update) and "Key properties" (bounded operator, prefix-scan depth);
+the "Your first delta model" tutorial, Step 5 "Adding time decay" (the decay
+contract: a per-event gap decays the carried state at the token boundary).
 The minGRU equations themselves (h_t = (1 - z_t) h_{t-1} + z_t g(p_t),
 z = sigma(k), g(x) = x + 1/2 for x >= 0 else sigma(x), [k, p] = x W_in, the
 identities log(1 - z) = -softplus(k)) are not printed on the pages; they are
@@ -32,4 +36,4 @@ the benchmark spec of the method and are written out here as given.
 Parity status of each function is listed in its module docstring.
 """
 
-from . import grad, logspace, metrics, minmax, mingru, scalar  # noqa: F401
+from . import decay, grad, logspace, metrics, minmax, mingru, scalar  # noqa: F401
