@@ -191,6 +191,39 @@ def leg_c3_backward(torch, sr, synth, steps, warmup):
     return res
 
 
+def leg_c3_decay(torch, sr, synth, steps, warmup):
+    """The headline scan shape with time decay of the carried state: k, p
+    (bf16) in, h (fp32) out as in the plain scan, plus one gap per (b, t) and
+    one rate per channel: 8 + 4/D algorithmic bytes per element."""
+    cfg = synth.CONFIGS[3]
+    B, T, D = cfg["B"], cfg["T"], cfg["D"]
+    log(f"[bench] c3 decayed B={B} T={T} D={D}")
+    kb = synth.device_normal(3, "k", (B, T, D), cfg["k_mean"], cfg["k_std"], torch.bfloat16)
+    pb = synth.device_normal(3, "p", (B, T, D), cfg["p_mean"], cfg["p_std"], torch.bfloat16)
+    h0 = synth.device_normal(3, "h0", (B, D))
+    rate = torch.from_numpy(synth.decay_rates(3, D)).cuda()
+    gap = torch.from_numpy(synth.gaps(3, B, T)).cuda()
+    sat = torch.zeros(1, dtype=torch.int32, device="cuda")
+    y = torch.empty((B, T, D), dtype=torch.float32, device="cuda")
+    ws = torch.empty(sr.raw_library().mingru_forward_workspace_size(B, T, 0, D, D, 0, 0),
+                     dtype=torch.uint8, device="cuda")
+    wall, mean_ms, _ = time_launches(
+        torch, lambda: sr.mingru_forward_decayed(k=kb, p=pb, h0=h0, decay_rate=rate, delta_t=gap,
+                                                 saturated=sat, workspace=ws, out=y),
+        steps, warmup)
+    if sr.workspace_status(ws) != 0 or not bool(torch.isfinite(y).all()):
+        raise RuntimeError("decayed scan: look-back expired or non-finite output")
+    n = B * T * D
+    alg = n * 8 + B * T * 4 + D * 4 + 2 * B * D * 4
+    res = dict(B=B, T=T, D=D, launch_ms_mean=mean_ms, elements_per_s=n / (wall / steps),
+               achieved_GBps=alg / (mean_ms * 1e-3) / 1e9,
+               frac_of_hbm_peak=alg / (mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+               saturated=int(sat.item()))
+    del kb, pb, y, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def leg_c5_backward(torch, sr, synth, steps, warmup):
     """Backward of the MinMax scan: reads r, s, x_out, dx, writes dr, ds
     (fp32): 24 algorithmic bytes per element."""
@@ -290,7 +323,7 @@ def main():
     # A fresh process reaches steady clocks only after a few hundred ms of
     # sustained load (measured: the first ~100 launches run 3-5% slower).
     ap.add_argument("--warmup", type=int, default=1000)
-    ap.add_argument("--legs", default="c3,c5,c3bwd,c5bwd,c4,c2,c1,copy")
+    ap.add_argument("--legs", default="c3,c5,c3bwd,c5bwd,c3decay,c4,c2,c1,copy")
     ap.add_argument("--cpu-steps", type=int, default=16384,
                     help="sequence prefix the CPU oracle baseline runs over (0 = skip)")
     ap.add_argument("--c4-steps", type=int, default=4096)
@@ -323,6 +356,8 @@ def main():
     if "c5bwd" in legs:
         extra["minmax_backward_b8_t32768_d192"] = leg_c5_backward(torch, sr, synth, args.steps,
                                                                   args.warmup)
+    if "c3decay" in legs:
+        extra["decayed_b8_t65536_d1024"] = leg_c3_decay(torch, sr, synth, args.steps, args.warmup)
     if "c2" in legs:
         extra["layer_b2_t1024_d512"] = leg_layer(torch, sr, synth, 2, 10)
     if "c1" in legs:

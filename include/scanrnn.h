@@ -116,6 +116,47 @@ sr_status mingru_step(int64_t B, int64_t D_in, int64_t D_h, int64_t D_out,
                       const float* h_prev, float* h_next, float* y_t,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Time decay of the carried state (the decay contract of the minGRU tutorial
+ * "Your first delta model", Step 5 "Adding time decay": each event comes with
+ * the gap delta_t preceding it; the carried state is scaled by gamma once per
+ * token, at the token boundary, before that token's own write; a zero gap is
+ * gamma = exp(0) = 1; a rate * gap above about 1e4 saturates float32 and
+ * wipes the memory, through a clamp, and is reported; log1p_delta compresses
+ * the gaps).  On the minGRU's vector state:
+ *
+ *     gap_t  = log1p(delta_t) if log1p_delta else delta_t
+ *     gamma  = exp(-min(decay_rate_d * gap_t, 1e4))
+ *     h_t    = (1 - z_t) (gamma_t h_{t-1}) + z_t g(p_t)
+ *
+ *   decay_rate  [D_h] fp32 per-channel rate, >= 0 and finite.
+ *   delta_t     [B,T] fp32 (sequence call) or [B] (step), contiguous, >= 0
+ *               and finite.  Other values are outside the contract.
+ *   log1p_delta 0 or 1.
+ *   saturated   device uint32 or NULL: set to 1 (atomic OR, never cleared by
+ *               the library) when some decay_rate_d * gap_t, rounded to fp32,
+ *               exceeds 1e4.  exp(-1e4) is 0 in fp32, so the clamp changes no
+ *               value; the flag says large gaps were not distinguished.
+ *
+ * Everything else is as in mingru_forward / mingru_step, with the same
+ * workspace sizes (mingru_forward_workspace_size, mingru_step_workspace_size).
+ */
+sr_status mingru_forward_decayed(int64_t B, int64_t T, int64_t D_in, int64_t D_h, int64_t D_out,
+                                 const float* x, const float* W_in,
+                                 const void* k, const void* p, int64_t ld_kp, sr_dtype kp_dtype,
+                                 const float* decay_rate, const float* delta_t, int log1p_delta,
+                                 uint32_t* saturated,
+                                 const float* h0, const float* W_out,
+                                 float* y, float* h_last,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+sr_status mingru_step_decayed(int64_t B, int64_t D_in, int64_t D_h, int64_t D_out,
+                              const float* x_t, const float* W_in, const float* W_out,
+                              const float* decay_rate, const float* delta_t, int log1p_delta,
+                              uint32_t* saturated,
+                              const float* h_prev, float* h_next, float* y_t,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
 /* Bytes of workspace minmax_scan needs. */
 size_t minmax_scan_workspace_size(int64_t B, int64_t T, int64_t D);
 

@@ -26,7 +26,9 @@ import torch
 __all__ = [
     "MinGRU",
     "mingru_forward",
+    "mingru_forward_decayed",
     "mingru_step",
+    "mingru_step_decayed",
     "minmax_scan",
     "mingru_scan_backward",
     "minmax_scan_backward",
@@ -51,6 +53,8 @@ EXPORTED = (
     "mingru_forward",
     "mingru_step_workspace_size",
     "mingru_step",
+    "mingru_forward_decayed",
+    "mingru_step_decayed",
     "minmax_scan_workspace_size",
     "minmax_scan",
     "minmax_step",
@@ -90,6 +94,12 @@ def _load() -> ctypes.CDLL:
     lib.mingru_step_workspace_size.argtypes = [i64, i64, i64, i64]
     lib.mingru_step.restype = i32
     lib.mingru_step.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.mingru_forward_decayed.restype = i32
+    lib.mingru_forward_decayed.argtypes = [i64, i64, i64, i64, i64, vp, vp, vp, vp, i64, i32,
+                                           vp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.mingru_step_decayed.restype = i32
+    lib.mingru_step_decayed.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp, vp, i32, vp, vp, vp,
+                                        vp, vp, sz, vp]
     lib.minmax_scan_workspace_size.restype = sz
     lib.minmax_scan_workspace_size.argtypes = [i64, i64, i64]
     lib.minmax_scan.restype = i32
@@ -165,6 +175,39 @@ def mingru_forward(x=None, W_in=None, *, k=None, p=None, h0=None, W_out=None,
     [D_h, D_out] the output projection (None = identity).  Returns y
     [B,T,D_out] fp32, and h_T [B,D_h] when ``return_last``.
     """
+    return _forward(x, W_in, k, p, h0, W_out, return_last, workspace, out, out_last, None)
+
+
+def mingru_forward_decayed(x=None, W_in=None, *, decay_rate, delta_t, log1p_delta=False,
+                           saturated=None, k=None, p=None, h0=None, W_out=None,
+                           return_last=False, workspace=None, out=None, out_last=None):
+    """``mingru_forward`` with time decay of the carried state: before token
+    t's write, h is scaled by exp(-min(decay_rate_d * gap_t, 1e4)), gap_t =
+    delta_t[b, t] (log1p of it with ``log1p_delta``).
+
+    ``decay_rate`` [D_h] fp32 (>= 0), ``delta_t`` [B,T] fp32 (>= 0, finite).
+    ``saturated``: an optional int32 GPU tensor of one element that the call
+    sets to 1 (never clears) when some rate * gap exceeds 1e4.
+    """
+    return _forward(x, W_in, k, p, h0, W_out, return_last, workspace, out, out_last,
+                    (decay_rate, delta_t, log1p_delta, saturated))
+
+
+def _decay_args(decay, D_h, gap_shape, device):
+    rate, gap, log1p, sat = decay
+    rate = _dev(rate, "decay_rate", shape=(D_h,))
+    gap = _dev(gap, "delta_t", shape=gap_shape)
+    if sat is not None:
+        sat = _dev(sat, "saturated", dtype=torch.int32)
+        if sat.numel() < 1 or not sat.is_contiguous():
+            raise ValueError("saturated must be a contiguous int32 tensor of at least one element")
+    for t, name in ((rate, "decay_rate"), (gap, "delta_t"), (sat, "saturated")):
+        if t is not None and t.device != device:
+            raise ValueError(f"{name} must be on {device}")
+    return rate, gap, int(bool(log1p)), sat
+
+
+def _forward(x, W_in, k, p, h0, W_out, return_last, workspace, out, out_last, decay):
     if W_in is not None:
         x = _dev(x, "x", ndim=3)
         W_in = _dev(W_in, "W_in", ndim=2)
@@ -224,11 +267,21 @@ def mingru_forward(x=None, W_in=None, *, k=None, p=None, h0=None, W_out=None,
     nbytes = _lib.mingru_forward_workspace_size(B, T, D_in, D_h, D_out, int(W_in is not None),
                                                 int(W_out is not None))
     ws = workspace if workspace is not None and workspace.numel() >= nbytes else _workspace(nbytes, device)
-    st = _lib.mingru_forward(B, T, D_in, D_h, D_out, _ptr(x if W_in is not None else None),
-                             _ptr(W_in), _ptr(kk), _ptr(pp), ld_kp, kp_dtype, _ptr(h0),
-                             _ptr(W_out), _ptr(y), _ptr(h_last), _ptr(ws), ws.numel(),
-                             _stream(device))
-    _check("mingru_forward", st)
+    if decay is None:
+        st = _lib.mingru_forward(B, T, D_in, D_h, D_out, _ptr(x if W_in is not None else None),
+                                 _ptr(W_in), _ptr(kk), _ptr(pp), ld_kp, kp_dtype, _ptr(h0),
+                                 _ptr(W_out), _ptr(y), _ptr(h_last), _ptr(ws), ws.numel(),
+                                 _stream(device))
+        _check("mingru_forward", st)
+    else:
+        rate, gap, log1p, sat = _decay_args(decay, D_h, (B, T), device)
+        st = _lib.mingru_forward_decayed(B, T, D_in, D_h, D_out,
+                                         _ptr(x if W_in is not None else None), _ptr(W_in),
+                                         _ptr(kk), _ptr(pp), ld_kp, kp_dtype, _ptr(rate),
+                                         _ptr(gap), log1p, _ptr(sat), _ptr(h0), _ptr(W_out),
+                                         _ptr(y), _ptr(h_last), _ptr(ws), ws.numel(),
+                                         _stream(device))
+        _check("mingru_forward_decayed", st)
     return (y, h_last) if return_last else y
 
 
@@ -239,6 +292,18 @@ def mingru_step(x_t, W_in, W_out=None, h_prev=None, h_next=None, workspace=None)
     same tensor as ``h_prev``) to avoid an allocation.  Without ``W_out`` the
     output is the new hidden state itself (the same tensor is returned twice).
     """
+    return _step(x_t, W_in, W_out, h_prev, h_next, workspace, None)
+
+
+def mingru_step_decayed(x_t, W_in, W_out=None, h_prev=None, h_next=None, workspace=None, *,
+                        decay_rate, delta_t, log1p_delta=False, saturated=None):
+    """``mingru_step`` with time decay: ``delta_t`` [B] is the gap preceding
+    this token (see ``mingru_forward_decayed``)."""
+    return _step(x_t, W_in, W_out, h_prev, h_next, workspace,
+                 (decay_rate, delta_t, log1p_delta, saturated))
+
+
+def _step(x_t, W_in, W_out, h_prev, h_next, workspace, decay):
     x_t = _dev(x_t, "x_t", ndim=2)
     W_in = _dev(W_in, "W_in", ndim=2)
     B, D_in = x_t.shape
@@ -269,10 +334,18 @@ def mingru_step(x_t, W_in, W_out=None, h_prev=None, h_next=None, workspace=None)
     ws = None
     if nbytes:
         ws = workspace if workspace is not None and workspace.numel() >= nbytes else _workspace(nbytes, device)
-    st = _lib.mingru_step(B, D_in, D_h, D_out, _ptr(x_t), _ptr(W_in), _ptr(W_out), _ptr(h_prev),
-                          _ptr(h_next), _ptr(y_t), _ptr(ws), 0 if ws is None else ws.numel(),
-                          _stream(device))
-    _check("mingru_step", st)
+    if decay is None:
+        st = _lib.mingru_step(B, D_in, D_h, D_out, _ptr(x_t), _ptr(W_in), _ptr(W_out),
+                              _ptr(h_prev), _ptr(h_next), _ptr(y_t), _ptr(ws),
+                              0 if ws is None else ws.numel(), _stream(device))
+        _check("mingru_step", st)
+    else:
+        rate, gap, log1p, sat = _decay_args(decay, D_h, (B,), device)
+        st = _lib.mingru_step_decayed(B, D_in, D_h, D_out, _ptr(x_t), _ptr(W_in), _ptr(W_out),
+                                      _ptr(rate), _ptr(gap), log1p, _ptr(sat), _ptr(h_prev),
+                                      _ptr(h_next), _ptr(y_t), _ptr(ws),
+                                      0 if ws is None else ws.numel(), _stream(device))
+        _check("mingru_step_decayed", st)
     return (h_next if y_t is None else y_t), h_next
 
 
@@ -398,10 +471,25 @@ class MinGRU:
     same shape.  ``layer(x_t, prev_hidden, return_next_prev_hidden=True)`` with
     a single token (x_t [B,dim] or [B,1,dim]) runs one step and returns
     (y_t, h_t); prev_hidden None is the zero state.
+
+    Time decay (the tutorials' decay contract): with ``decay_rate`` (a float
+    or a [dim*expansion] tensor of per-channel rates >= 0), a call may pass
+    ``delta_t`` -- [B,T] gaps for a sequence, [B] for one token -- and the
+    carried state is scaled by exp(-min(rate * gap, 1e4)) before each
+    token's write (gap = log1p(delta_t) with ``log1p_delta``).  Without
+    ``delta_t`` a call does not decay.  The first call whose rate * gap
+    exceeds 1e4 raises one UserWarning per layer (checking synchronises the
+    stream; ``warn_saturation=False`` skips the check).
     """
 
+    SATURATION_WARNING = (
+        "delta_t gaps exceed the decay clamp (decay_rate * delta_t > 1e4): those tokens "
+        "wipe the carried state, and gaps beyond the clamp are no longer told apart; "
+        "pass log1p_delta=True or rescale delta_t to keep them distinct")
+
     def __init__(self, dim: int, expansion: float = 1.0, W_in=None, W_out=None,
-                 device="cuda", generator=None):
+                 device="cuda", generator=None, decay_rate=None, log1p_delta=False,
+                 warn_saturation=True):
         self.dim = int(dim)
         self.dim_inner = int(dim * expansion)
         if W_in is None:
@@ -410,18 +498,53 @@ class MinGRU:
             W_out = torch.randn(self.dim_inner, self.dim, generator=generator) / self.dim_inner ** 0.5
         self.W_in = W_in.to(device=device, dtype=torch.float32).contiguous()
         self.W_out = None if W_out is False else W_out.to(device=device, dtype=torch.float32).contiguous()
+        self.decay_rate = None
+        if decay_rate is not None:
+            rate = torch.as_tensor(decay_rate, dtype=torch.float32)
+            self.decay_rate = rate.expand(self.dim_inner).to(device).contiguous()
+        self.log1p_delta = bool(log1p_delta)
+        self.warn_saturation = bool(warn_saturation)
+        self._saturated = None
+        self._warned = False
 
-    def __call__(self, x, prev_hidden=None, return_next_prev_hidden=False):
+    def _decay(self, delta_t):
+        if self.decay_rate is None or delta_t is None:
+            return None
+        if self._saturated is None:
+            self._saturated = torch.zeros(1, dtype=torch.int32, device=self.W_in.device)
+        return dict(decay_rate=self.decay_rate, delta_t=delta_t.to(torch.float32),
+                    log1p_delta=self.log1p_delta, saturated=self._saturated)
+
+    def _maybe_warn(self, dec):
+        if dec is None or self._warned or not self.warn_saturation:
+            return
+        if int(self._saturated.item()) != 0:
+            import warnings
+            self._warned = True
+            warnings.warn(self.SATURATION_WARNING, UserWarning, stacklevel=3)
+
+    def __call__(self, x, prev_hidden=None, return_next_prev_hidden=False, delta_t=None):
         single = x.dim() == 2 or (x.dim() == 3 and x.shape[1] == 1 and prev_hidden is not None)
+        dec = self._decay(delta_t)
         if single:
             x_t = x.reshape(x.shape[0], x.shape[-1])
             h = None if prev_hidden is None else prev_hidden.reshape(x_t.shape[0], self.dim_inner)
-            y_t, h_t = mingru_step(x_t, self.W_in, self.W_out, h)
+            if dec is None:
+                y_t, h_t = mingru_step(x_t, self.W_in, self.W_out, h)
+            else:
+                dec["delta_t"] = dec["delta_t"].reshape(x_t.shape[0])
+                y_t, h_t = mingru_step_decayed(x_t, self.W_in, self.W_out, h, **dec)
+            self._maybe_warn(dec)
             if x.dim() == 3:
                 y_t = y_t.unsqueeze(1)
             return (y_t, h_t) if return_next_prev_hidden else y_t
         h0 = None
         if prev_hidden is not None:
             h0 = prev_hidden.reshape(x.shape[0], self.dim_inner)
-        y, h_last = mingru_forward(x, self.W_in, h0=h0, W_out=self.W_out, return_last=True)
+        if dec is None:
+            y, h_last = mingru_forward(x, self.W_in, h0=h0, W_out=self.W_out, return_last=True)
+        else:
+            y, h_last = mingru_forward_decayed(x, self.W_in, h0=h0, W_out=self.W_out,
+                                               return_last=True, **dec)
+        self._maybe_warn(dec)
         return (y, h_last) if return_next_prev_hidden else y

@@ -70,39 +70,30 @@ sr_status check_workspace(void* ws, size_t have, size_t need) {
     if (!(cond)) return fail(SR_ERR_INVALID_ARGUMENT, __VA_ARGS__); \
   } while (0)
 
-}  // namespace
+// Time decay of the carried state: the rate per channel, the gap per token.
+struct Decay {
+  const float* rate;
+  const float* delta_t;
+  int log1p_delta;
+  uint32_t* saturated;
+};
 
-sr_status fail(sr_status code, const char* fmt, ...) {
-  va_list ap;
-  va_start(ap, fmt);
-  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
-  va_end(ap);
-  return code;
+// n_rate channels need a rate and n_gap tokens a gap.
+sr_status check_decay(const Decay& d, int64_t n_rate, int64_t n_gap) {
+  SR_REQUIRE(n_rate == 0 || d.rate != nullptr, "decay_rate is NULL");
+  SR_REQUIRE(n_gap == 0 || d.delta_t != nullptr, "delta_t is NULL");
+  SR_REQUIRE(d.log1p_delta == 0 || d.log1p_delta == 1, "log1p_delta must be 0 or 1 (got %d)",
+             d.log1p_delta);
+  SR_REQUIRE(aligned(d.rate, 4) && aligned(d.delta_t, 4) && aligned(d.saturated, 4),
+             "decay pointers must be 4-byte aligned");
+  return SR_OK;
 }
 
-}  // namespace sr
-
-using namespace sr;
-
-extern "C" {
-
-const char* scanrnn_last_error(void) { return g_last_error; }
-
-const char* scanrnn_version(void) { return "0.1.0"; }
-
-size_t mingru_forward_workspace_size(int64_t B, int64_t T, int64_t D_in, int64_t D_h,
-                                     int64_t D_out, int has_w_in, int has_w_out) {
-  int64_t n;
-  if (B < 0 || T < 0 || D_in < 0 || D_h < 0 || D_out < 0 || !prod3(B, T, 2 * D_h, &n)) return 0;
-  return forward_layout(B, T, D_in, D_h, D_out, has_w_in != 0, has_w_out != 0).total;
-}
-
-sr_status mingru_forward(int64_t B, int64_t T, int64_t D_in, int64_t D_h, int64_t D_out,
-                         const float* x, const float* W_in, const void* k, const void* p,
-                         int64_t ld_kp, sr_dtype kp_dtype, const float* h0, const float* W_out,
-                         float* y, float* h_last, void* workspace, size_t workspace_bytes,
-                         void* stream) {
-  g_last_error[0] = '\0';
+sr_status forward_impl(int64_t B, int64_t T, int64_t D_in, int64_t D_h, int64_t D_out,
+                       const float* x, const float* W_in, const void* k, const void* p,
+                       int64_t ld_kp, sr_dtype kp_dtype, const float* h0, const float* W_out,
+                       float* y, float* h_last, void* workspace, size_t workspace_bytes,
+                       void* stream, const Decay* dec) {
   SR_REQUIRE(B >= 0 && T >= 0 && D_in >= 0 && D_h >= 0 && D_out >= 0,
              "sizes must be non-negative (B=%lld T=%lld D_in=%lld D_h=%lld D_out=%lld)",
              (long long)B, (long long)T, (long long)D_in, (long long)D_h, (long long)D_out);
@@ -130,6 +121,10 @@ sr_status mingru_forward(int64_t B, int64_t T, int64_t D_in, int64_t D_h, int64_
     SR_REQUIRE(aligned(k, esz) && aligned(p, esz), "k and p must be aligned to their element size");
     int64_t span;
     SR_REQUIRE(prod3(B, T, ld_kp, &span), "k/p extent overflows int64");
+  }
+  if (dec != nullptr) {
+    sr_status st = check_decay(*dec, n_h > 0 ? D_h : 0, n_h > 0 ? B * T : 0);
+    if (st != SR_OK) return st;
   }
   const FwdLayout L = forward_layout(B, T, D_in, D_h, D_out, w_in, w_out);
   sr_status st = check_workspace(workspace, workspace_bytes, L.total);
@@ -164,6 +159,12 @@ sr_status mingru_forward(int64_t B, int64_t T, int64_t D_in, int64_t D_h, int64_
   rq.last = h_last;
   rq.workspace = ws;
   rq.stream = s;
+  if (dec != nullptr) {
+    rq.decay_rate = dec->rate;
+    rq.delta_t = dec->delta_t;
+    rq.log1p_delta = dec->log1p_delta;
+    rq.saturated = dec->saturated;
+  }
   st = launch_scan(rq);
   if (st != SR_OK) return st;
   if (w_out && T > 0)
@@ -171,17 +172,10 @@ sr_status mingru_forward(int64_t B, int64_t T, int64_t D_in, int64_t D_h, int64_
   return st;
 }
 
-size_t mingru_step_workspace_size(int64_t B, int64_t D_in, int64_t D_h, int64_t D_out) {
-  int64_t n;
-  if (B < 0 || D_in < 0 || D_h < 0 || D_out < 0 || !prod3(B, 2 * D_h + D_out, D_in + D_h + 1, &n))
-    return 0;
-  return step_workspace(B, D_in, D_h, D_out);
-}
-
-sr_status mingru_step(int64_t B, int64_t D_in, int64_t D_h, int64_t D_out, const float* x_t,
-                      const float* W_in, const float* W_out, const float* h_prev, float* h_next,
-                      float* y_t, void* workspace, size_t workspace_bytes, void* stream) {
-  g_last_error[0] = '\0';
+sr_status step_impl(int64_t B, int64_t D_in, int64_t D_h, int64_t D_out, const float* x_t,
+                    const float* W_in, const float* W_out, const float* h_prev, float* h_next,
+                    float* y_t, void* workspace, size_t workspace_bytes, void* stream,
+                    const Decay* dec) {
   SR_REQUIRE(B >= 0 && D_in >= 0 && D_h >= 0 && D_out >= 0,
              "sizes must be non-negative (B=%lld D_in=%lld D_h=%lld D_out=%lld)", (long long)B,
              (long long)D_in, (long long)D_h, (long long)D_out);
@@ -200,17 +194,99 @@ sr_status mingru_step(int64_t B, int64_t D_in, int64_t D_h, int64_t D_out, const
   SR_REQUIRE(aligned(x_t, 4) && aligned(W_in, 4) && aligned(W_out, 4) && aligned(h_prev, 4) &&
                  aligned(h_next, 4) && aligned(y_t, 4),
              "fp32 pointers must be 4-byte aligned");
+  if (dec != nullptr) {
+    sr_status st = check_decay(*dec, n_h > 0 ? D_h : 0, n_h > 0 ? B : 0);
+    if (st != SR_OK) return st;
+  }
   sr_status st = check_workspace(workspace, workspace_bytes, step_workspace(B, D_in, D_h, D_out));
   if (st != SR_OK) return st;
   if (B == 0) return SR_OK;
   hipStream_t s = as_stream(stream);
   float* g_buf = static_cast<float*>(workspace);
-  st = launch_step_in(B, D_in, D_h, x_t, W_in, h_prev, h_next, g_buf, s);
+  StepDecay sd{};
+  if (dec != nullptr) sd = StepDecay{dec->rate, dec->delta_t, dec->log1p_delta, dec->saturated};
+  st = launch_step_in(B, D_in, D_h, x_t, W_in, h_prev, h_next, g_buf, s,
+                      dec != nullptr ? &sd : nullptr);
   if (st != SR_OK) return st;
   if (W_out != nullptr)
     return launch_gemm_f32(B, D_out, D_h, h_next, D_h, W_out, D_out, y_t, D_out, g_buf, s);
   if (y_t != nullptr && y_t != h_next) return launch_copy_or_zero(y_t, h_next, n_h, s);
   return SR_OK;
+}
+
+}  // namespace
+
+sr_status fail(sr_status code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+}  // namespace sr
+
+using namespace sr;
+
+extern "C" {
+
+const char* scanrnn_last_error(void) { return g_last_error; }
+
+const char* scanrnn_version(void) { return "0.1.0"; }
+
+size_t mingru_forward_workspace_size(int64_t B, int64_t T, int64_t D_in, int64_t D_h,
+                                     int64_t D_out, int has_w_in, int has_w_out) {
+  int64_t n;
+  if (B < 0 || T < 0 || D_in < 0 || D_h < 0 || D_out < 0 || !prod3(B, T, 2 * D_h, &n)) return 0;
+  return forward_layout(B, T, D_in, D_h, D_out, has_w_in != 0, has_w_out != 0).total;
+}
+
+sr_status mingru_forward(int64_t B, int64_t T, int64_t D_in, int64_t D_h, int64_t D_out,
+                         const float* x, const float* W_in, const void* k, const void* p,
+                         int64_t ld_kp, sr_dtype kp_dtype, const float* h0, const float* W_out,
+                         float* y, float* h_last, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  g_last_error[0] = '\0';
+  return forward_impl(B, T, D_in, D_h, D_out, x, W_in, k, p, ld_kp, kp_dtype, h0, W_out, y, h_last,
+                      workspace, workspace_bytes, stream, nullptr);
+}
+
+sr_status mingru_forward_decayed(int64_t B, int64_t T, int64_t D_in, int64_t D_h, int64_t D_out,
+                                 const float* x, const float* W_in, const void* k, const void* p,
+                                 int64_t ld_kp, sr_dtype kp_dtype, const float* decay_rate,
+                                 const float* delta_t, int log1p_delta, uint32_t* saturated,
+                                 const float* h0, const float* W_out, float* y, float* h_last,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error[0] = '\0';
+  const Decay dec{decay_rate, delta_t, log1p_delta, saturated};
+  return forward_impl(B, T, D_in, D_h, D_out, x, W_in, k, p, ld_kp, kp_dtype, h0, W_out, y, h_last,
+                      workspace, workspace_bytes, stream, &dec);
+}
+
+size_t mingru_step_workspace_size(int64_t B, int64_t D_in, int64_t D_h, int64_t D_out) {
+  int64_t n;
+  if (B < 0 || D_in < 0 || D_h < 0 || D_out < 0 || !prod3(B, 2 * D_h + D_out, D_in + D_h + 1, &n))
+    return 0;
+  return step_workspace(B, D_in, D_h, D_out);
+}
+
+sr_status mingru_step(int64_t B, int64_t D_in, int64_t D_h, int64_t D_out, const float* x_t,
+                      const float* W_in, const float* W_out, const float* h_prev, float* h_next,
+                      float* y_t, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error[0] = '\0';
+  return step_impl(B, D_in, D_h, D_out, x_t, W_in, W_out, h_prev, h_next, y_t, workspace,
+                   workspace_bytes, stream, nullptr);
+}
+
+sr_status mingru_step_decayed(int64_t B, int64_t D_in, int64_t D_h, int64_t D_out,
+                              const float* x_t, const float* W_in, const float* W_out,
+                              const float* decay_rate, const float* delta_t, int log1p_delta,
+                              uint32_t* saturated, const float* h_prev, float* h_next, float* y_t,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error[0] = '\0';
+  const Decay dec{decay_rate, delta_t, log1p_delta, saturated};
+  return step_impl(B, D_in, D_h, D_out, x_t, W_in, W_out, h_prev, h_next, y_t, workspace,
+                   workspace_bytes, stream, &dec);
 }
 
 size_t minmax_scan_workspace_size(int64_t B, int64_t T, int64_t D) {

@@ -42,6 +42,11 @@ struct GemmParams {
   int64_t D_h;
   const float* h_prev;
   float* h_next;
+  // step mode with time decay of the carried state (rate null: none)
+  const float* rate;     // [D_h]
+  const float* gap;      // [M] gap preceding the token, per row
+  int log1p_gap;
+  uint32_t* saturated;   // or null: OR-ed with 1 when a rate * gap exceeds the clamp
   // split-K: blockIdx.z covers K rows [z*k_split, (z+1)*k_split); with
   // `partial` set, raw tile sums go to partial[z][M][Ncols] for a reduction.
   int64_t k_split;
@@ -81,11 +86,23 @@ __device__ __forceinline__ float g_act(float p) {
 }
 
 // h_next = (1 - z) h_prev + z g(p) with z = sigma(k), for one (row, channel).
+// With time decay the carried state is first scaled by
+// exp(-min(rate_d * gap_row, 1e4)) (the token boundary comes before the
+// token's write; exp(-1e4) is zero in float32, so the clamp changes no value
+// and only marks saturation).
 __device__ __forceinline__ void step_update(const GemmParams& P, int64_t row, int64_t d, float k,
                                             float p) {
   float a;
   const float z = sigmoid_pos_neg(k, a);
-  const float hp = P.h_prev ? P.h_prev[row * P.D_h + d] : 0.0f;
+  float hp = P.h_prev ? P.h_prev[row * P.D_h + d] : 0.0f;
+  if (P.rate != nullptr) {
+    constexpr float kClamp = 1.0e4f, kLog2e = 1.4426950408889634f;
+    const float gap = P.log1p_gap ? log1pf(P.gap[row]) : P.gap[row];
+    const float e = P.rate[d] * gap;
+    if (e > kClamp && P.saturated != nullptr)
+      __hip_atomic_fetch_or(P.saturated, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    hp *= __builtin_amdgcn_exp2f(fminf(e, kClamp) * -kLog2e);
+  }
   P.h_next[row * P.D_h + d] = fmaf(a, hp, z * g_act(p));
 }
 
@@ -313,12 +330,18 @@ sr_status launch_gemm_f32(int64_t M, int64_t N, int64_t K, const float* A, int64
 
 sr_status launch_step_in(int64_t Bsz, int64_t D_in, int64_t D_h, const float* x_t,
                          const float* W_in, const float* h_prev, float* h_next, float* ws,
-                         hipStream_t stream) {
+                         hipStream_t stream, const StepDecay* decay) {
   if (Bsz == 0 || D_h == 0) return SR_OK;
   GemmParams P{};
   P.M = Bsz; P.N = 2 * D_h; P.K = D_in;
   P.A = x_t; P.lda = D_in; P.Bm = W_in; P.ldb = 2 * D_h; P.C = nullptr; P.ldc = 0;
   P.D_h = D_h; P.h_prev = h_prev; P.h_next = h_next;
+  if (decay != nullptr) {
+    P.rate = decay->rate;
+    P.gap = decay->gap;
+    P.log1p_gap = decay->log1p_gap;
+    P.saturated = decay->saturated;
+  }
   P.ncols = 2 * D_h;
   return launch_mode(kStep, P, (Bsz + BM - 1) / BM, (D_h + BN / 2 - 1) / (BN / 2), ws, stream);
 }

@@ -50,6 +50,11 @@ struct ScanRequest {
   float* last;         // [B,D] or nullptr
   void* workspace;
   hipStream_t stream;
+  // Time decay of the carried state (minGRU only; none when decay_rate is null).
+  const float* decay_rate = nullptr;  // [D]
+  const float* delta_t = nullptr;     // [B,T], contiguous
+  int log1p_delta = 0;
+  uint32_t* saturated = nullptr;      // device flag, OR-ed with 1 on saturation
 };
 
 sr_status launch_scan(const ScanRequest& rq);
@@ -89,12 +94,21 @@ sr_status launch_gemm_f32(int64_t M, int64_t N, int64_t K,
                           const float* Bm, int64_t ldb,
                           float* C, int64_t ldc, float* ws, hipStream_t stream);
 
-// Step kernel: h_next = (1 - z) h_prev + z g(p) with [k|p] = x_t W_in,
-// computed as one GEMM whose epilogue applies the update.  `ws`: as above
-// with gemm_workspace_bytes(Bsz, 2*D_h, D_in, true).
+// Time decay of the carried state in the step (see mingru_step_decayed).
+struct StepDecay {
+  const float* rate;     // [D_h]
+  const float* gap;      // [Bsz]
+  int log1p_gap;
+  uint32_t* saturated;   // or null
+};
+
+// Step kernel: h_next = (1 - z) gamma h_prev + z g(p) with [k|p] = x_t W_in
+// (gamma = 1 without decay), computed as one GEMM whose epilogue applies the
+// update.  `ws`: as above with gemm_workspace_bytes(Bsz, 2*D_h, D_in, true).
 sr_status launch_step_in(int64_t Bsz, int64_t D_in, int64_t D_h,
                          const float* x_t, const float* W_in,
-                         const float* h_prev, float* h_next, float* ws, hipStream_t stream);
+                         const float* h_prev, float* h_next, float* ws, hipStream_t stream,
+                         const StepDecay* decay = nullptr);
 
 // Number of K slices a GEMM of this shape uses, and the workspace they need.
 int gemm_splits(int64_t M, int64_t N, int64_t K, bool step);

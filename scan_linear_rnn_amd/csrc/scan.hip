@@ -82,7 +82,7 @@ sr_status reset_workspace(void* ws, size_t used, hipStream_t stream) {
 namespace {
 using namespace eng;
 
-template <class Op, typename TIn, int V>
+template <class Op, typename TIn, int V, bool kDecay>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd)))
 void chunk_scan_kernel(const ScanParams P) {
   constexpr int N = kElemsPerLane / V;
@@ -120,11 +120,35 @@ void chunk_scan_kernel(const ScanParams P) {
   const rsrc_t r1 = make_rsrc(static_cast<const TIn*>(P.in1) + base_el, (end_el - base_el) * esz);
   const int voff_in = int(lane * V * esz);
   const int row_bytes = int(P.ld_in * esz);
+  // Time decay: -rate * log2(e) for each of the lane's channels, and the gap
+  // of step n of the run held by lane n (one load per wave; the step's gap
+  // is then read from that lane, so it is uniform across the wave).  Rates
+  // past D and gaps past T are zero: no decay, no saturation.  Issued before
+  // the input loads so that the first step does not wait for all of them.
+  float nrate[V];
+  float gap_l = 0.0f, gap_max = 0.0f;
+  typename Raw<float, V>::type rate_raw{};
+  if constexpr (kDecay) {
+    // Buffer loads throughout: channels past D, lanes >= N and steps past T
+    // fall outside the descriptors' extents and read zero, with no branch
+    // (a branch around a load would make the wave wait for it right there).
+    const int64_t n_gaps = P.T - tw < N ? (P.T - tw > 0 ? P.T - tw : 0) : N;
+    const rsrc_t rg = make_rsrc(P.gap + (tw < P.T ? b * P.T + tw : 0), n_gaps * 4);
+    gap_l = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, lane * 4, 0, 0));
+    const rsrc_t rr = make_rsrc(P.rate + dtile_first, (P.D - dtile_first) * 4);
+    rate_raw = Raw<float, V>::load(rr, lane * V * 4, 0);
+  }
   typename R::type raw0[N], raw1[N];
 #pragma unroll
   for (int n = 0; n < N; ++n) {
     raw0[n] = R::load(r0, voff_in, n * row_bytes);
     raw1[n] = R::load(r1, voff_in, n * row_bytes);
+  }
+  if constexpr (kDecay) {
+    if (P.log1p_gap) gap_l = log1pf(gap_l);  // after the input loads are issued
+    Raw<float, V>::unpack(rate_raw, nrate);
+#pragma unroll
+    for (int c = 0; c < V; ++c) nrate[c] *= kNegLog2e;
   }
   Pair e[N][V];
   Pair agg[V];
@@ -142,6 +166,12 @@ void chunk_scan_kernel(const ScanParams P) {
     R::unpack(raw1[n], x1);
 #pragma unroll
     for (int c = 0; c < V; ++c) e[n][c] = Op::element(x0[c], x1[c]);
+    if constexpr (kDecay) {
+      const float gn = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gap_l), n));
+      gap_max = fmaxf(gap_max, gn);
+#pragma unroll
+      for (int c = 0; c < V; ++c) e[n][c].u *= __builtin_amdgcn_exp2f(nrate[c] * gn);
+    }
     if (n < nvalid) {
 #pragma unroll
       for (int c = 0; c < V; ++c) agg[c] = Op::compose(agg[c], e[n][c]);
@@ -153,6 +183,15 @@ void chunk_scan_kernel(const ScanParams P) {
   if (!lane_on) {
 #pragma unroll
     for (int c = 0; c < V; ++c) agg[c] = Op::identity();
+  }
+  if constexpr (kDecay) {
+    if (P.saturated != nullptr) {
+      bool sat = false;
+#pragma unroll
+      for (int c = 0; c < V; ++c) sat = sat || (d + c < P.D && P.rate[d + c] * gap_max > kDecayClamp);
+      if (__builtin_amdgcn_ballot_w64(sat) != 0 && lane == 0)
+        __hip_atomic_fetch_or(P.saturated, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 #pragma unroll
   for (int c = 0; c < V; ++c) s_pre[wave][lane * V + c] = agg[c];
@@ -199,17 +238,17 @@ __global__ void copy_or_zero_kernel(float* dst, const float* src, int64_t n) {
     dst[i] = src ? src[i] : 0.0f;
 }
 
-template <class Op, typename TIn, int V>
+template <class Op, typename TIn, int V, bool kDecay>
 hipError_t launch_v(const ScanParams& P, hipStream_t stream) {
   const int64_t n_blocks = P.n_chains * P.n_tchunks;
-  hipLaunchKernelGGL((chunk_scan_kernel<Op, TIn, V>), dim3(uint32_t(n_blocks)),
+  hipLaunchKernelGGL((chunk_scan_kernel<Op, TIn, V, kDecay>), dim3(uint32_t(n_blocks)),
                      dim3(64 * kWaves), 0, stream, P);
   return hipGetLastError();
 }
 
-template <class Op, typename TIn>
+template <class Op, typename TIn, bool kDecay = false>
 hipError_t launch_op(int V, const ScanParams& P, hipStream_t stream) {
-  return V == 2 ? launch_v<Op, TIn, 2>(P, stream) : launch_v<Op, TIn, 1>(P, stream);
+  return V == 2 ? launch_v<Op, TIn, 2, kDecay>(P, stream) : launch_v<Op, TIn, 1, kDecay>(P, stream);
 }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -293,13 +332,22 @@ sr_status launch_scan(const ScanRequest& rq) {
   P.counter = reinterpret_cast<uint32_t*>(ws);
   P.status = reinterpret_cast<uint32_t*>(ws) + 1;
   P.state = reinterpret_cast<uint64_t*>(ws + kHeaderBytes);
+  P.rate = rq.decay_rate;
+  P.gap = rq.delta_t;
+  P.log1p_gap = rq.log1p_delta;
+  P.saturated = rq.saturated;
 
   const size_t used = kHeaderBytes + size_t(g.n_tchunks) * size_t(rq.B) * size_t(rq.D) * 8;
   sr_status st = reset_workspace(ws, used, rq.stream);
   if (st != SR_OK) return st;
   hipError_t err;
+  const bool decay = rq.decay_rate != nullptr;
   if (rq.op == ScanOp::kMinMax)
     err = launch_op<MinMaxOp, float>(g.V, P, rq.stream);
+  else if (decay && rq.in_dtype == SR_BF16)
+    err = launch_op<MinGRUOp, uint16_t, true>(g.V, P, rq.stream);
+  else if (decay)
+    err = launch_op<MinGRUOp, float, true>(g.V, P, rq.stream);
   else if (rq.in_dtype == SR_BF16)
     err = launch_op<MinGRUOp, uint16_t>(g.V, P, rq.stream);
   else

@@ -169,7 +169,22 @@ struct ScanParams {
   uint32_t* counter;  // header word 0: ticket counter
   uint32_t* status;   // header word 1: timeout flag
   uint64_t* state;    // [n_tchunks][B][D] look-back words
+  // Time decay of the carried state (minGRU only; unused when rate is null).
+  const float* rate;     // [D] per-channel decay rate
+  const float* gap;      // [B,T] gap preceding each token
+  int log1p_gap;         // gaps are compressed with log1p first
+  uint32_t* saturated;   // or null: OR-ed with 1 when a rate * gap exceeds the clamp
 };
+
+// Time decay (the decay contract of the minGRU tutorials' "Adding time decay"
+// step): the carried state is scaled by exp(-min(rate * gap, kDecayClamp))
+// at the token boundary, before the token's own write.  exp(-x) is already
+// zero in float32 for x above ~104, so the clamp changes no value and is not
+// applied; it marks where large gaps stop being distinguishable, which is
+// reported as saturation.  For rate >= 0, rounding is monotone in the gap, so
+// some rate * gap_n exceeds the clamp exactly when rate * max_n gap_n does.
+constexpr float kDecayClamp = 1.0e4f;
+constexpr float kNegLog2e = -1.4426950408889634f;
 
 // Look-back along T for one channel, one tile at a time: used when the
 // window fetched in one round trip holds no usable end state.  Returns the

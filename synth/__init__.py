@@ -11,8 +11,10 @@ from .inputs import (  # noqa: F401
     TENSOR_IDS,
     T_BLOCK,
     bf16_round,
+    decay_rates,
     device_normal,
     device_uniform,
+    gaps,
     normal_bt,
     normal_mat,
     normal_vec,

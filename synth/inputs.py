@@ -37,6 +37,8 @@ TENSOR_IDS = {
     "r": 6,
     "s": 7,
     "x0": 8,
+    "decay_rate": 9,
+    "delta_t": 10,
 }
 
 # The five workloads (config index = position + 1).  "N(0, 1/D)" names a
@@ -123,6 +125,33 @@ def normal_vec(cfg: int, name: str, B: int, D: int, mean: float = 0.0,
 
 def uniform_vec(cfg: int, name: str, B: int, D: int, lo: float, hi: float) -> np.ndarray:
     return _no_negative_zero(_rng(cfg, name).uniform(lo, hi, (B, D)).astype(np.float32))
+
+
+def decay_rates(cfg: int, D: int, lo: float = 1e-3, hi: float = 1e-1) -> np.ndarray:
+    """float32 [D] per-channel decay rates, log-uniform on [lo, hi] (time
+    constants from 1/hi to 1/lo tokens)."""
+    u = _rng(cfg, "decay_rate").uniform(np.log10(lo), np.log10(hi), D)
+    return (10.0 ** u).astype(np.float32)
+
+
+def gaps(cfg: int, B: int, T: int, mean: float = 1.0, p_huge: float = 1e-3,
+         huge: float = 1e6, t0: int = 0) -> np.ndarray:
+    """float32 [B, T] gaps preceding each token, drawn per T-block: exponential
+    with the given mean (irregular event times), except that a fraction
+    ``p_huge`` of them is ``huge`` (long silences; with rates above
+    1e4 / huge they saturate the decay)."""
+    if t0 % T_BLOCK:
+        raise ValueError("t0 must be a multiple of T_BLOCK")
+    out = np.empty((B, T), dtype=np.float32)
+    tb0 = t0 // T_BLOCK
+    for i in range(-(-T // T_BLOCK)):
+        a = i * T_BLOCK
+        n = min(T_BLOCK, T - a)
+        rng = _rng(cfg, "delta_t", tb0 + i)
+        blk = rng.exponential(mean, (B, T_BLOCK))
+        blk[rng.random((B, T_BLOCK)) < p_huge] = huge
+        out[:, a:a + n] = blk[:, :n].astype(np.float32)
+    return out
 
 
 def _torch_gen(cfg: int, name: str, device) -> torch.Generator:

@@ -126,3 +126,40 @@ def test_python_binding_rejects_cpu_tensors():
         sr.minmax_scan(x, x, torch.zeros(2, 4))
     with pytest.raises((ValueError, TypeError)):
         sr.mingru_forward(k=x, p=x)
+
+
+def _fwd_decayed(**kw):
+    args = dict(B=2, T=8, D_in=0, D_h=4, D_out=4, x=None, W_in=None, k=FAKE, p=FAKE2,
+                ld_kp=4, kp_dtype=sr.SR_F32, rate=FAKE, gap=FAKE2, log1p=0, sat=None,
+                h0=None, W_out=None, y=FAKE, h_last=None, ws=FAKE, ws_bytes=16, stream=None)
+    args.update(kw)
+    return lib.mingru_forward_decayed(
+        args["B"], args["T"], args["D_in"], args["D_h"], args["D_out"], args["x"], args["W_in"],
+        args["k"], args["p"], args["ld_kp"], args["kp_dtype"], args["rate"], args["gap"],
+        args["log1p"], args["sat"], args["h0"], args["W_out"], args["y"], args["h_last"],
+        args["ws"], args["ws_bytes"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(rate=None), sr.SR_ERR_INVALID_ARGUMENT),
+    (dict(gap=None), sr.SR_ERR_INVALID_ARGUMENT),
+    (dict(log1p=2), sr.SR_ERR_INVALID_ARGUMENT),
+    (dict(rate=ctypes.c_void_p(0x10002)), sr.SR_ERR_INVALID_ARGUMENT),
+    (dict(sat=ctypes.c_void_p(0x10003)), sr.SR_ERR_INVALID_ARGUMENT),
+    (dict(k=None), sr.SR_ERR_INVALID_ARGUMENT),          # the undecayed checks still apply
+    (dict(), sr.SR_ERR_WORKSPACE_TOO_SMALL),             # valid decay arguments: reaches sizing
+])
+def test_forward_decayed_rejects_bad_arguments(kw, code):
+    assert _fwd_decayed(**kw) == code
+    assert lib.scanrnn_last_error()
+
+
+def test_step_decayed_rejects_bad_arguments():
+    f = lib.mingru_step_decayed
+    need = lib.mingru_step_workspace_size(256, 2048, 2048, 2048)
+    args = [256, 2048, 2048, 2048, FAKE, FAKE, FAKE]
+    tail = [FAKE, FAKE, FAKE, FAKE, need - 1, None]   # h_prev, h_next, y_t, ws, bytes, stream
+    assert f(*args, None, FAKE, 0, None, *tail) == sr.SR_ERR_INVALID_ARGUMENT
+    assert f(*args, FAKE, None, 0, None, *tail) == sr.SR_ERR_INVALID_ARGUMENT
+    assert f(*args, FAKE, FAKE, 5, None, *tail) == sr.SR_ERR_INVALID_ARGUMENT
+    assert f(*args, FAKE, FAKE, 1, None, *tail) == sr.SR_ERR_WORKSPACE_TOO_SMALL

@@ -1,0 +1,215 @@
+"""GPU parity of the time-decayed minGRU scan and step against the fp64 oracle."""
+
+import warnings
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import decay, metrics
+from tests.gpu_util import TOL_F32, dev, host64, say
+from tests import pins_decay
+
+pytestmark = pytest.mark.gpu
+
+sr = pytest.importorskip("scan_linear_rnn_amd")
+
+
+def _case(B, T, D, seed, huge=False):
+    rng = np.random.default_rng([1200, seed])
+    k = rng.normal(-1.0, 1.5, (B, T, D)).astype(np.float32)
+    p = rng.standard_normal((B, T, D)).astype(np.float32)
+    h0 = rng.standard_normal((B, D)).astype(np.float32)
+    lam = (10.0 ** rng.uniform(-3, 0, D)).astype(np.float32)
+    dt = rng.exponential(1.0, (B, T)).astype(np.float32)
+    dt[rng.random((B, T)) < 0.05] = 0.0
+    if huge:
+        dt[rng.random((B, T)) < 0.01] = 1e6
+    return k, p, h0, lam, dt
+
+
+def _err(h, k, p, lam, dt, h0, log1p):
+    ref = decay.scan(k, p, lam, dt, h0, log1p)
+    carry, inp = decay.scan_terms(k, p, lam, dt, h0, log1p)
+    return metrics.h_rel_err(host64(h), ref, carry, inp)
+
+
+@pytest.mark.parametrize("B,T,D,with_h0,log1p,huge", [
+    (2, 64, 16, False, False, False),
+    (3, 1000, 200, True, False, True),
+    (2, 5000, 384, True, True, True),
+    (1, 1, 8, True, False, False),
+    (4, 333, 7, False, True, False),
+    (1, 7000, 130, True, False, True),
+])
+def test_decayed_scan_f32(B, T, D, with_h0, log1p, huge):
+    say(f"decay f32 B={B} T={T} D={D} h0={with_h0} log1p={log1p} huge={huge}")
+    k, p, h0, lam, dt = _case(B, T, D, seed=B * 7 + T + D, huge=huge)
+    h0 = h0 if with_h0 else None
+    sat = torch.zeros(1, dtype=torch.int32, device="cuda")
+    h, last = sr.mingru_forward_decayed(k=dev(k), p=dev(p), h0=None if h0 is None else dev(h0),
+                                        decay_rate=dev(lam), delta_t=dev(dt), log1p_delta=log1p,
+                                        saturated=sat, return_last=True)
+    err = _err(h, k, p, lam, dt, h0, log1p)
+    say("error", err)
+    assert err < TOL_F32
+    assert torch.equal(last, h[:, -1])
+    assert int(sat.item()) == int(decay.saturated(lam, dt, log1p))
+
+
+def test_decayed_scan_bf16_reduced_c3():
+    cfg = synth.CONFIGS[3]
+    B, T, D = 2, 4096, 1024
+    say("decay bf16 reduced C3")
+    kb = synth.bf16_round(synth.normal_bt(3, "k", B, T, D, cfg["k_mean"], cfg["k_std"])).cuda()
+    pb = synth.bf16_round(synth.normal_bt(3, "p", B, T, D, cfg["p_mean"], cfg["p_std"])).cuda()
+    h0 = synth.normal_vec(3, "h0", B, D)
+    lam = synth.decay_rates(3, D)
+    dt = synth.gaps(3, B, T)
+    sat = torch.zeros(1, dtype=torch.int32, device="cuda")
+    h = sr.mingru_forward_decayed(k=kb, p=pb, h0=dev(h0), decay_rate=dev(lam), delta_t=dev(dt),
+                                  saturated=sat)
+    err = _err(h, kb.double().cpu().numpy(), pb.double().cpu().numpy(), lam, dt, h0, False)
+    say("error", err)
+    assert err < TOL_F32
+    assert int(sat.item()) == int(decay.saturated(lam, dt)) == 1
+
+
+def test_zero_gaps_equal_undecayed_bitwise():
+    B, T, D = 2, 3000, 256
+    k, p, h0, lam, _ = _case(B, T, D, seed=1201)
+    kd, pd, h0d = dev(k), dev(p), dev(h0)
+    plain = sr.mingru_forward(k=kd, p=pd, h0=h0d)
+    dec = sr.mingru_forward_decayed(k=kd, p=pd, h0=h0d, decay_rate=dev(lam),
+                                    delta_t=torch.zeros((B, T), device="cuda"))
+    assert torch.equal(plain, dec)
+    dec0 = sr.mingru_forward_decayed(k=kd, p=pd, h0=h0d, decay_rate=torch.zeros(D, device="cuda"),
+                                     delta_t=dev(np.full((B, T), 3.0, np.float32)))
+    assert torch.equal(plain, dec0)
+
+
+def test_saturating_gap_restarts_the_state():
+    """A gap far past the clamp wipes the carried state: from that token on,
+    h equals a fresh scan of the remaining tokens (within rounding, as the
+    tiles fall differently), and the flag is set; with log1p_delta the same
+    gaps do not saturate."""
+    B, T, D = 2, 9000, 192
+    k, p, h0, lam, dt = _case(B, T, D, seed=1202)
+    lam = np.maximum(lam, np.float32(0.05))
+    tstar = 4321
+    dt[:, tstar] = 1e7
+    sat = torch.zeros(1, dtype=torch.int32, device="cuda")
+    kd, pd, lamd = dev(k), dev(p), dev(lam)
+    h = sr.mingru_forward_decayed(k=kd, p=pd, h0=dev(h0), decay_rate=lamd, delta_t=dev(dt),
+                                  saturated=sat)
+    assert int(sat.item()) == 1
+    dt_fresh = dt[:, tstar:].copy()
+    dt_fresh[:, 0] = 0.0
+    fresh = sr.mingru_forward_decayed(k=kd[:, tstar:].contiguous(), p=pd[:, tstar:].contiguous(),
+                                      decay_rate=lamd, delta_t=dev(dt_fresh))
+    ref = decay.scan(k[:, tstar:], p[:, tstar:], lam, dt_fresh)
+    assert metrics.max_abs_rel(host64(h[:, tstar:]), ref) < 1e-5
+    assert metrics.max_abs_rel(host64(fresh), ref) < 1e-5
+    sat.zero_()
+    sr.mingru_forward_decayed(k=kd, p=pd, h0=dev(h0), decay_rate=lamd, delta_t=dev(dt),
+                              log1p_delta=True, saturated=sat)
+    assert int(sat.item()) == 0
+
+
+def test_page_example_through_the_layer():
+    """The tutorial's Step 5 run, on the minGRU layer: the same token six
+    times, gaps [0, 1, 1, 20000, 1, 1] against all-zero gaps, the state read
+    after each prefix.  The gapped state after events 3, 4, 5 repeats events
+    0, 1, 2 bit for bit; control equals the undecayed layer; one warning
+    over the whole trajectory, none with log1p_delta."""
+    D = 8
+    g = torch.Generator().manual_seed(0)
+    rate = torch.rand(D, generator=g) * 1.4 + 0.6        # rate * 20000 > 1e4 everywhere
+    layer = sr.MinGRU(D, decay_rate=rate, generator=g)
+    x = torch.randn(1, 1, D, generator=g).expand(1, 6, D).contiguous().cuda()
+    gapped = torch.tensor([pins_decay.PAGE_GAPS]).cuda()
+    control = torch.zeros_like(gapped)
+
+    def trajectory(lyr, delta_t):
+        states = []
+        with warnings.catch_warnings(record=True) as caught:
+            warnings.simplefilter("always")
+            for t in range(1, 7):
+                _, h = lyr(x[:, :t], delta_t=delta_t[:, :t], return_next_prev_hidden=True)
+                states.append(h.clone())
+        return torch.stack(states, 1)[0], list(caught)
+
+    hg, wg = trajectory(layer, gapped)
+    ctl = sr.MinGRU(D, W_in=layer.W_in, W_out=layer.W_out, decay_rate=rate)
+    hc, wc = trajectory(ctl, control)
+    assert len(wg) == 1 and issubclass(wg[0].category, UserWarning) and not wc
+    assert torch.equal(hg[3:6], hg[0:3])
+    assert torch.equal(hg[0], hc[0])
+    _, plain = sr.MinGRU(D, W_in=layer.W_in, W_out=layer.W_out)(x, return_next_prev_hidden=True)
+    assert torch.equal(hc[5], plain[0])
+    ng, nc = hg.norm(dim=1), hc.norm(dim=1)
+    assert bool((nc[1:] >= nc[:-1]).all()) and bool((ng[1:3] < nc[1:3]).all())
+    soft = sr.MinGRU(D, W_in=layer.W_in, W_out=layer.W_out, decay_rate=rate, log1p_delta=True)
+    _, ws = trajectory(soft, gapped)
+    assert not ws
+
+
+def test_decayed_step_loop_matches_oracle():
+    """Token by token with W_in / W_out (the step kernel's epilogue applies
+    the decay), against the oracle's step, carrying h between calls."""
+    rng = np.random.default_rng(1203)
+    B, T, D_in, D_h = 4, 40, 96, 160
+    x = rng.standard_normal((B, T, D_in)).astype(np.float32)
+    W_in = (rng.standard_normal((D_in, 2 * D_h)) / D_in ** 0.5).astype(np.float32)
+    W_out = (rng.standard_normal((D_h, D_h)) / D_h ** 0.5).astype(np.float32)
+    lam = (10.0 ** rng.uniform(-2, 0, D_h)).astype(np.float32)
+    dt = rng.exponential(1.0, (B, T)).astype(np.float32)
+    dt[:, 17] = 1e6
+    sat = torch.zeros(1, dtype=torch.int32, device="cuda")
+    Wi, Wo, lamd, dtd = dev(W_in), dev(W_out), dev(lam), dev(dt)
+    h = None
+    h_ref = None
+    for t in range(T):
+        y_t, h = sr.mingru_step_decayed(dev(x[:, t]), Wi, Wo, h, decay_rate=lamd,
+                                        delta_t=dtd[:, t].contiguous(), log1p_delta=False,
+                                        saturated=sat)
+        y_ref, h_ref = decay.step(x[:, t], W_in, lam, dt[:, t], W_out, h_ref)
+        assert metrics.max_abs_rel(host64(h), h_ref) < 1e-4, t
+        assert metrics.y_rel_err(host64(y_t), y_ref, h_ref, W_out) < 1e-4, t
+        h_ref = host64(h)   # carry the GPU state, so each step is checked on its own
+    assert int(sat.item()) == 1
+    # The whole-sequence call on the same inputs agrees with the oracle too.
+    y, last = sr.mingru_forward_decayed(dev(x), Wi, W_out=Wo, decay_rate=lamd, delta_t=dtd,
+                                        return_last=True)
+    y_ref, hs_ref, _ = decay.layer(x, W_in, lam, dt, W_out)
+    assert metrics.y_rel_err(host64(y), y_ref, hs_ref, W_out) < 1e-4
+
+
+def test_full_c3_size_decayed_sampled():
+    cfg = synth.CONFIGS[3]
+    B, T, D = cfg["B"], cfg["T"], cfg["D"]
+    say("decay full C3")
+    kb = synth.device_normal(3, "k", (B, T, D), cfg["k_mean"], cfg["k_std"], torch.bfloat16)
+    pb = synth.device_normal(3, "p", (B, T, D), cfg["p_mean"], cfg["p_std"], torch.bfloat16)
+    h0 = synth.device_normal(3, "h0", (B, D))
+    lam = synth.decay_rates(3, D)
+    dt = synth.gaps(3, B, T)
+    sat = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = torch.empty(sr.raw_library().mingru_forward_workspace_size(B, T, 0, D, D, 0, 0),
+                     dtype=torch.uint8, device="cuda")
+    h = sr.mingru_forward_decayed(k=kb, p=pb, h0=h0, decay_rate=dev(lam), delta_t=dev(dt),
+                                  saturated=sat, workspace=ws)
+    assert sr.workspace_status(ws) == 0
+    assert int(sat.item()) == 1
+    rng = np.random.default_rng(1204)
+    bs = rng.integers(0, B, 12)
+    ds = rng.integers(0, D, 12)
+    errs = []
+    for b, d in zip(bs, ds):
+        kc = kb[b, :, d].double().cpu().numpy()[None, :, None]
+        pc = pb[b, :, d].double().cpu().numpy()[None, :, None]
+        h0c = h0[b, d].double().cpu().numpy().reshape(1, 1)
+        errs.append(_err(h[b, :, d][None, :, None], kc, pc, lam[d:d + 1], dt[b:b + 1], h0c, False))
+    say("sampled errors", max(errs))
+    assert max(errs) < TOL_F32
