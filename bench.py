@@ -324,7 +324,7 @@ def main():
     # sustained load (measured: the first ~100 launches run 3-5% slower).
     ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--legs", default="c3,c5,c3bwd,c5bwd,c3decay,c4,c2,c1,copy")
-    ap.add_argument("--cpu-steps", type=int, default=16384,
+    ap.add_argument("--cpu-steps", type=int, default=65536,
                     help="sequence prefix the CPU oracle baseline runs over (0 = skip)")
     ap.add_argument("--c4-steps", type=int, default=4096)
     args = ap.parse_args()
