@@ -25,7 +25,7 @@ OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libscanrnn.so")
 
 ARCH = "gfx950"
-SOURCES = ["scan.hip", "scan_bwd.hip", "gemm.hip", "api.cpp"]
+SOURCES = ["scan.hip", "scan_bwd.hip", "gemm.hip", "fused.hip", "api.cpp"]
 COMMON = [
     f"--offload-arch={ARCH}",
     "-O3",

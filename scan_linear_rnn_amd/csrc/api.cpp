@@ -33,17 +33,20 @@ struct FwdLayout {
 };
 
 // Workspace of a forward call: the scan's look-back words, the staged [k|p]
-// and h when the projections run, and split-K partial sums of the GEMMs.
+// (unless the projection is fused into the scan) and h when the projections
+// run, and split-K partial sums of the GEMMs.
 FwdLayout forward_layout(int64_t B, int64_t T, int64_t D_in, int64_t D_h, int64_t D_out,
                          bool w_in, bool w_out) {
   FwdLayout L{};
-  L.scan_bytes = align_up(scan_workspace_bytes(B, T, D_h), kAlign);
+  const bool fused = w_in && fused_forward_applies(B, T, D_h);
+  L.scan_bytes = align_up(fused ? fused_workspace_bytes(B, T, D_h) : scan_workspace_bytes(B, T, D_h),
+                          kAlign);
   L.kp_off = L.scan_bytes;
-  L.kp_bytes = w_in ? align_up(size_t(B) * size_t(T) * size_t(2 * D_h) * 4, kAlign) : 0;
+  L.kp_bytes = w_in && !fused ? align_up(size_t(B) * size_t(T) * size_t(2 * D_h) * 4, kAlign) : 0;
   L.h_off = L.kp_off + L.kp_bytes;
   L.h_bytes = w_out ? align_up(size_t(B) * size_t(T) * size_t(D_h) * 4, kAlign) : 0;
   L.g_off = L.h_off + L.h_bytes;
-  const size_t g_in = w_in ? gemm_workspace_bytes(B * T, 2 * D_h, D_in, false) : 0;
+  const size_t g_in = w_in && !fused ? gemm_workspace_bytes(B * T, 2 * D_h, D_in, false) : 0;
   const size_t g_out = w_out ? gemm_workspace_bytes(B * T, D_out, D_h, false) : 0;
   L.g_bytes = g_in > g_out ? g_in : g_out;
   L.total = L.g_off + L.g_bytes;
@@ -140,6 +143,30 @@ sr_status forward_impl(int64_t B, int64_t T, int64_t D_in, int64_t D_h, int64_t 
     // No channels: y has no elements unless D_out > 0 with W_out (then y = 0).
     if (w_out && n_y > 0) return launch_copy_or_zero(y, nullptr, n_y, s);
     return SR_OK;
+  }
+  if (w_in && T > 0 && fused_forward_applies(B, T, D_h)) {
+    FusedRequest fr{};
+    fr.B = B;
+    fr.T = T;
+    fr.D_in = D_in;
+    fr.D_h = D_h;
+    fr.x = x;
+    fr.W_in = W_in;
+    fr.h0 = h0;
+    fr.h = h_buf;
+    fr.h_last = h_last;
+    fr.workspace = ws;
+    fr.stream = s;
+    if (dec != nullptr) {
+      fr.decay_rate = dec->rate;
+      fr.delta_t = dec->delta_t;
+      fr.log1p_delta = dec->log1p_delta;
+      fr.saturated = dec->saturated;
+    }
+    st = launch_fused_forward(fr);
+    if (st != SR_OK) return st;
+    if (w_out) st = launch_gemm_f32(B * T, D_out, D_h, h_buf, D_h, W_out, D_out, y, D_out, g_buf, s);
+    return st;
   }
   if (w_in && T > 0) {
     st = launch_gemm_f32(B * T, 2 * D_h, D_in, x, D_in, W_in, 2 * D_h, kp_buf, 2 * D_h, g_buf, s);

@@ -1,0 +1,215 @@
+// Fused input projection and minGRU scan for gfx950: [k | p] = x W_in is
+// computed a tile at a time on the matrix cores and scanned in the same
+// workgroup, so k and p never travel to HBM and back (16 bytes per element
+// in fp32).  The minGRU profile's parallel mode, with the layer's projection
+// feeding the scan directly.
+//
+// A workgroup owns 128 consecutive steps of one batch row and 64 channels:
+// the 128 x 128 MFMA tile of gemm_tile.hpp with paired columns, so lane
+// (kl, ml) of wave (wm, wn) holds k and p of channel 32*wn + ml for the 32
+// rows wm*64 + 32*i + 8*q + 4*kl + j (i, j, q in 0..1, 0..3, 0..3).  The scan
+// of the tile runs on that layout:
+//   1. each lane turns its 32 (k, p) into maps, in the accumulator
+//      registers, and composes each run of 4 consecutive rows (8 runs);
+//   2. along T the runs of a wave alternate between lane ml and lane ml + 32
+//      (run 2n + kl of the wave's 64 rows is run n of lane kl), so the two
+//      lanes swap their runs and both walk the 16 runs in order, each keeping
+//      the prefix that enters its own runs;
+//   3. the two wave halves along T (wm = 0, 1) meet in LDS and the tile is
+//      linked to its predecessors along T by the engine's windowed look-back
+//      (scan_engine.hpp), exactly as in the stand-alone scan;
+//   4. each lane replays its maps from the state entering its runs and stores
+//      h.
+// Tiles take tickets in execution order, so a tile only waits on tiles that
+// are already running (see scan.hip).  Time decay (the minGRU tutorials'
+// "Adding time decay" step) scales each map's coefficient by
+// exp(-rate_d * gap_t) as in the stand-alone scan.
+
+#include "gemm_tile.hpp"
+#include "scan_engine.hpp"
+
+namespace sr {
+namespace {
+
+using namespace gt;
+using namespace eng;
+
+constexpr int kTileT = BM;     // steps per tile
+constexpr int kTileD = BN / 2; // channels per tile (paired k / p columns)
+
+struct FusedParams {
+  GemmParams g;  // A = x [B*T, D_in], Bm = W_in [D_in, 2*D_h], K = D_in
+  ScanParams s;  // look-back context; out = h [B,T,D_h], D = D_h
+};
+
+template <bool kDecay>
+__global__ __launch_bounds__(256) void fused_proj_scan_kernel(const FusedParams F) {
+  __shared__ float As[2][BK][BM + PAD];
+  __shared__ float Bs[2][BK][BN + PAD];
+  __shared__ uint32_t s_ticket;
+  __shared__ Pair s_pre[2][kTileD];
+  __shared__ uint64_t s_win[kWindowTiles][kTileD];
+  __shared__ float s_hin[kTileD];
+  __shared__ float s_gap[kTileT];
+
+  const ScanParams& P = F.s;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int kl = lane >> 5, ml = lane & 31;
+  const uint32_t ticket = take_ticket(P, &s_ticket);
+  const Tile tl = decode_ticket(P, ticket, kTileD);
+  const int64_t t0 = tl.tchunk * kTileT;
+  const int64_t rows = P.T - t0 < kTileT ? P.T - t0 : kTileT;
+  const int c = wn * 32 + ml;  // channel within the tile
+  const int64_t d = tl.d0 + c;
+  const bool chan_ok = d < P.D;
+
+  float rate = 0.0f, nrate = 0.0f;
+  if constexpr (kDecay) {
+    if (tid < kTileT) {
+      float gp = tid < rows ? P.gap[tl.b * P.T + t0 + tid] : 0.0f;
+      if (P.log1p_gap) gp = log1pf(gp);
+      s_gap[tid] = gp;  // published by the K loop's barriers
+    }
+    rate = chan_ok ? P.rate[d] : 0.0f;
+    nrate = rate * kNegLog2e;
+  }
+
+  floatx16 acc[2][2];
+  tile_mainloop<kStep>(F.g, tl.b * P.T + t0, rows, tl.d0, 0, F.g.K, As, Bs, acc);
+
+  // 1. Maps in place of the sums (set 0 <- coefficient, set 1 <- offset);
+  // rows past T become the identity.  Then the runs of 4 rows: run n = (i, q),
+  // n = 4*i + q.
+  bool sat = false;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int lr = wm * 64 + i * 32 + (r / 4) * 8 + kl * 4 + (r % 4);
+      Pair m = MinGRUOp::element(acc[i][0][r], acc[i][1][r]);
+      if constexpr (kDecay) {
+        const float gp = s_gap[lr];
+        m.u *= __builtin_amdgcn_exp2f(nrate * gp);
+        sat = sat || (rate * gp > kDecayClamp);
+      }
+      if (lr >= rows) m = MinGRUOp::identity();
+      acc[i][0][r] = m.u;
+      acc[i][1][r] = m.v;
+    }
+  }
+  if constexpr (kDecay) {
+    if (P.saturated != nullptr && __builtin_amdgcn_ballot_w64(sat) != 0 && lane == 0)
+      __hip_atomic_fetch_or(P.saturated, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  Pair mine[8];
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+    const int i = n / 4, q = n % 4;
+    Pair m = {acc[i][0][4 * q], acc[i][1][4 * q]};
+#pragma unroll
+    for (int j = 1; j < 4; ++j)
+      m = MinGRUOp::compose(m, Pair{acc[i][0][4 * q + j], acc[i][1][4 * q + j]});
+    mine[n] = m;
+  }
+  // 2. The partner lane's runs (lane ^ 32), then the prefix over the wave's
+  // 16 runs in T order: run 2n is lane kl = 0's run n, run 2n + 1 lane 1's.
+  Pair pre[8];
+  Pair run = MinGRUOp::identity();
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+    const Pair other = {__shfl_xor(mine[n].u, 32), __shfl_xor(mine[n].v, 32)};
+    const Pair even = kl == 0 ? mine[n] : other;
+    const Pair odd = kl == 0 ? other : mine[n];
+    if (kl == 0) pre[n] = run;
+    run = MinGRUOp::compose(run, even);
+    if (kl == 1) pre[n] = run;
+    run = MinGRUOp::compose(run, odd);
+  }
+  // 3. Wave halves along T, then the look-back across tiles.
+  if (kl == 0) s_pre[wm][c] = run;
+  __syncthreads();
+  resolve_tile<MinGRUOp, 2, kTileD, 256>(P, tl, s_pre, s_win, s_hin);
+
+  // 4. Replay and store.
+  const float h_wave = MinGRUOp::apply(s_pre[wm][c], s_hin[c]);
+  float* out = P.out + (tl.b * P.T + t0) * P.D + d;
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+    const int i = n / 4, q = n % 4;
+    float h = MinGRUOp::apply(pre[n], h_wave);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int lr = wm * 64 + i * 32 + q * 8 + kl * 4 + j;
+      h = MinGRUOp::apply(Pair{acc[i][0][4 * q + j], acc[i][1][4 * q + j]}, h);
+      if (chan_ok && lr < rows) {
+        out[int64_t(lr) * P.D] = h;
+        if (P.last != nullptr && t0 + lr == P.T - 1) P.last[tl.b * P.D + d] = h;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+bool fused_forward_applies(int64_t B, int64_t T, int64_t D_h) {
+  // Worth it when the tiles alone fill the part several times over; smaller
+  // problems keep the split-K projection, which spreads its K loop over more
+  // workgroups.
+  if (B <= 0 || T <= 0 || D_h <= 0) return false;
+  const int64_t tiles = B * ((D_h + kTileD - 1) / kTileD) * ((T + kTileT - 1) / kTileT);
+  return tiles >= 1024 && tiles * 256 <= int64_t(0xFFFFFFFFu);
+}
+
+size_t fused_workspace_bytes(int64_t B, int64_t T, int64_t D_h) {
+  const int64_t n_tchunks = (T + kTileT - 1) / kTileT;
+  return eng::kHeaderBytes + align_up(size_t(n_tchunks) * size_t(B) * size_t(D_h) * 8, kAlign);
+}
+
+sr_status launch_fused_forward(const FusedRequest& rq) {
+  FusedParams F{};
+  GemmParams& g = F.g;
+  g.M = rq.B * rq.T;
+  g.N = 2 * rq.D_h;
+  g.K = rq.D_in;
+  g.A = rq.x;
+  g.lda = rq.D_in;
+  g.Bm = rq.W_in;
+  g.ldb = 2 * rq.D_h;
+  g.D_h = rq.D_h;
+  ScanParams& P = F.s;
+  P.out = rq.h;
+  P.init = rq.h0;
+  P.last = rq.h_last;
+  P.B = rq.B;
+  P.T = rq.T;
+  P.D = rq.D_h;
+  P.n_dtiles = (rq.D_h + kTileD - 1) / kTileD;
+  P.n_tchunks = (rq.T + kTileT - 1) / kTileT;
+  P.n_chains = rq.B * P.n_dtiles;
+  char* ws = static_cast<char*>(rq.workspace);
+  P.counter = reinterpret_cast<uint32_t*>(ws);
+  P.status = reinterpret_cast<uint32_t*>(ws) + 1;
+  P.state = reinterpret_cast<uint64_t*>(ws + eng::kHeaderBytes);
+  P.rate = rq.decay_rate;
+  P.gap = rq.delta_t;
+  P.log1p_gap = rq.log1p_delta;
+  P.saturated = rq.saturated;
+  const int64_t tiles = P.n_chains * P.n_tchunks;
+  const size_t used = eng::kHeaderBytes + size_t(P.n_tchunks) * size_t(rq.B) * size_t(rq.D_h) * 8;
+  sr_status st = eng::reset_workspace(ws, used, rq.stream);
+  if (st != SR_OK) return st;
+  if (rq.decay_rate != nullptr)
+    hipLaunchKernelGGL(fused_proj_scan_kernel<true>, dim3(uint32_t(tiles)), dim3(256), 0,
+                       rq.stream, F);
+  else
+    hipLaunchKernelGGL(fused_proj_scan_kernel<false>, dim3(uint32_t(tiles)), dim3(256), 0,
+                       rq.stream, F);
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return fail(SR_ERR_HIP, "fused projection + scan launch: %s", hipGetErrorString(err));
+  return SR_OK;
+}
+
+}  // namespace sr

@@ -62,6 +62,29 @@ sr_status launch_scan(const ScanRequest& rq);
 // Chooses the geometry a request will use (exposed for sizing and tests).
 ScanGeometry choose_geometry(const ScanRequest& rq);
 
+// Fused input projection + scan (fused.hip): h = scan(x W_in), the [k|p]
+// tile never leaving the workgroup.  Used for large enough problems (see
+// fused_forward_applies); its workspace is the look-back words of its own
+// 128-step tiles.
+struct FusedRequest {
+  int64_t B, T, D_in, D_h;
+  const float* x;      // [B,T,D_in]
+  const float* W_in;   // [D_in, 2*D_h]
+  const float* h0;     // [B,D_h] or nullptr
+  float* h;            // [B,T,D_h]
+  float* h_last;       // [B,D_h] or nullptr
+  void* workspace;
+  hipStream_t stream;
+  const float* decay_rate = nullptr;  // time decay, as in ScanRequest
+  const float* delta_t = nullptr;
+  int log1p_delta = 0;
+  uint32_t* saturated = nullptr;
+};
+
+bool fused_forward_applies(int64_t B, int64_t T, int64_t D_h);
+size_t fused_workspace_bytes(int64_t B, int64_t T, int64_t D_h);
+sr_status launch_fused_forward(const FusedRequest& rq);
+
 // Backward pass of a scan (reverse time, same engine).
 struct BackwardRequest {
   ScanOp op;

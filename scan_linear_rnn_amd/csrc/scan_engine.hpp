@@ -252,8 +252,10 @@ __device__ __forceinline__ Tile decode_ticket(const ScanParams& P, uint32_t tick
 // it applied one by one in order, gives the state entering the tile, written
 // to s_hin; only if the window holds no usable end state does a thread walk
 // back tile by tile.  The tile's end state is published last.  Ends with a
-// barrier, after which s_pre and s_hin are ready for phase 3.
-template <class Op, int W, int Dc>
+// barrier, after which s_pre and s_hin are ready for phase 3.  W is the
+// number of segments along T (waves of the scan kernel), NT the number of
+// threads in the workgroup (a multiple of Dc, at least Dc).
+template <class Op, int W, int Dc, int NT = 64 * W>
 __device__ __forceinline__ void resolve_tile(const ScanParams& P, const Tile& tl,
                                              Pair (&s_pre)[W][Dc],
                                              uint64_t (&s_win)[kWindowTiles][Dc],
@@ -283,7 +285,8 @@ __device__ __forceinline__ void resolve_tile(const ScanParams& P, const Tile& tl
     // one round trip; position -1 stands for the initial state.
     const int c = tid % Dc;
     const int64_t dd = tl.d0 + c;
-    for (int q = tid / Dc; q < kWin; q += (64 * W) / Dc) {
+    static_assert(NT % Dc == 0 && NT >= Dc, "one or more full sets of channel threads");
+    for (int q = tid / Dc; q < kWin; q += NT / Dc) {
       const int64_t m = tl.tchunk - 1 - q;
       uint64_t w = pack_state(__uint_as_float(kCanonNaN));
       if (dd < P.D) {
