@@ -4,10 +4,10 @@
 // in fp32).  The minGRU profile's parallel mode, with the layer's projection
 // feeding the scan directly.
 //
-// A workgroup owns 128 consecutive steps of one batch row and 64 channels:
-// the 128 x 128 MFMA tile of gemm_tile.hpp with paired columns, so lane
-// (kl, ml) of wave (wm, wn) holds k and p of channel 32*wn + ml for the 32
-// rows wm*64 + 32*i + 8*q + 4*kl + j (i, j, q in 0..1, 0..3, 0..3).  The scan
+// A workgroup owns 256 consecutive steps of one batch row and 64 channels:
+// the 256 x 128 MFMA tile of gemm_tile.hpp (8 waves) with paired columns, so
+// lane (kl, ml) of wave (wm, wn) holds k and p of channel 32*wn + ml for the
+// 32 rows wm*64 + 32*i + 8*q + 4*kl + j (i, j, q in 0..1, 0..3, 0..3).  The scan
 // of the tile runs on that layout:
 //   1. each lane turns its 32 (k, p) into maps, in the accumulator
 //      registers, and composes each run of 4 consecutive rows (8 runs);
@@ -15,7 +15,7 @@
 //      (run 2n + kl of the wave's 64 rows is run n of lane kl), so the two
 //      lanes swap their runs and both walk the 16 runs in order, each keeping
 //      the prefix that enters its own runs;
-//   3. the two wave halves along T (wm = 0, 1) meet in LDS and the tile is
+//   3. the four wave rows along T (wm = 0..3) meet in LDS and the tile is
 //      linked to its predecessors along T by the engine's windowed look-back
 //      (scan_engine.hpp), exactly as in the stand-alone scan;
 //   4. each lane replays its maps from the state entering its runs and stores
@@ -34,7 +34,7 @@ namespace {
 using namespace gt;
 using namespace eng;
 
-constexpr int kTileT = BM;     // steps per tile
+constexpr int kTileT = 256;    // steps per tile (the 256-row GEMM tile)
 constexpr int kTileD = BN / 2; // channels per tile (paired k / p columns)
 
 struct FusedParams {
@@ -42,12 +42,17 @@ struct FusedParams {
   ScanParams s;  // look-back context; out = h [B,T,D_h], D = D_h
 };
 
+// Register budget: 4 waves per SIMD (two workgroups per CU), as the plain
+// 256-row GEMM runs.  The scan epilogue then spills a few dozen registers,
+// once per tile; measured 17.3 ms against 19.1 ms at the compiler's own
+// choice (2 waves per SIMD) on the config-4 prefill projection.
 template <bool kDecay>
-__global__ __launch_bounds__(256) void fused_proj_scan_kernel(const FusedParams F) {
-  __shared__ float As[2][BK][BM + PAD];
+__global__ __launch_bounds__(2 * kTileT) __attribute__((amdgpu_waves_per_eu(4)))
+void fused_proj_scan_kernel(const FusedParams F) {
+  __shared__ float As[2][BK][kTileT + PAD];
   __shared__ float Bs[2][BK][BN + PAD];
   __shared__ uint32_t s_ticket;
-  __shared__ Pair s_pre[2][kTileD];
+  __shared__ Pair s_pre[kTileT / 64][kTileD];
   __shared__ uint64_t s_win[kWindowTiles][kTileD];
   __shared__ float s_hin[kTileD];
   __shared__ float s_gap[kTileT];
@@ -78,7 +83,7 @@ __global__ __launch_bounds__(256) void fused_proj_scan_kernel(const FusedParams 
   }
 
   floatx16 acc[2][2];
-  tile_mainloop<kStep>(F.g, tl.b * P.T + t0, rows, tl.d0, 0, F.g.K, As, Bs, acc);
+  tile_mainloop<kStep, kTileT>(F.g, tl.b * P.T + t0, rows, tl.d0, 0, F.g.K, As, Bs, acc);
 
   // 1. Maps in place of the sums (set 0 <- coefficient, set 1 <- offset);
   // rows past T become the identity.  Then the runs of 4 rows: run n = (i, q),
@@ -128,10 +133,10 @@ __global__ __launch_bounds__(256) void fused_proj_scan_kernel(const FusedParams 
     if (kl == 1) pre[n] = run;
     run = MinGRUOp::compose(run, odd);
   }
-  // 3. Wave halves along T, then the look-back across tiles.
+  // 3. Wave rows along T, then the look-back across tiles.
   if (kl == 0) s_pre[wm][c] = run;
   __syncthreads();
-  resolve_tile<MinGRUOp, 2, kTileD, 256>(P, tl, s_pre, s_win, s_hin);
+  resolve_tile<MinGRUOp, kTileT / 64, kTileD, 2 * kTileT>(P, tl, s_pre, s_win, s_hin);
 
   // 4. Replay and store.
   const float h_wave = MinGRUOp::apply(s_pre[wm][c], s_hin[c]);
@@ -160,7 +165,7 @@ bool fused_forward_applies(int64_t B, int64_t T, int64_t D_h) {
   // workgroups.
   if (B <= 0 || T <= 0 || D_h <= 0) return false;
   const int64_t tiles = B * ((D_h + kTileD - 1) / kTileD) * ((T + kTileT - 1) / kTileT);
-  return tiles >= 1024 && tiles * 256 <= int64_t(0xFFFFFFFFu);
+  return tiles >= 512 && tiles * 2 * kTileT <= int64_t(0xFFFFFFFFu);
 }
 
 size_t fused_workspace_bytes(int64_t B, int64_t T, int64_t D_h) {
@@ -202,10 +207,10 @@ sr_status launch_fused_forward(const FusedRequest& rq) {
   sr_status st = eng::reset_workspace(ws, used, rq.stream);
   if (st != SR_OK) return st;
   if (rq.decay_rate != nullptr)
-    hipLaunchKernelGGL(fused_proj_scan_kernel<true>, dim3(uint32_t(tiles)), dim3(256), 0,
+    hipLaunchKernelGGL(fused_proj_scan_kernel<true>, dim3(uint32_t(tiles)), dim3(2 * kTileT), 0,
                        rq.stream, F);
   else
-    hipLaunchKernelGGL(fused_proj_scan_kernel<false>, dim3(uint32_t(tiles)), dim3(256), 0,
+    hipLaunchKernelGGL(fused_proj_scan_kernel<false>, dim3(uint32_t(tiles)), dim3(2 * kTileT), 0,
                        rq.stream, F);
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return fail(SR_ERR_HIP, "fused projection + scan launch: %s", hipGetErrorString(err));

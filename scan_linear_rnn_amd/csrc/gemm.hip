@@ -52,21 +52,25 @@ __device__ __forceinline__ void step_update(const GemmParams& P, int64_t row, in
   P.h_next[row * P.D_h + d] = fmaf(a, hp, z * g_act(p));
 }
 
-template <int MODE>
-__global__ __launch_bounds__(256) void gemm_f32_kernel(const GemmParams P) {
-  __shared__ float As[2][BK][BM + PAD];
+// One TBM x 128 tile per workgroup; blockIdx.x numbers the tiles (N tiles
+// fastest, so consecutive tiles share their A rows; renumbered per XCD),
+// blockIdx.z the K slice.
+template <int MODE, int TBM>
+__global__ __launch_bounds__(2 * TBM) void gemm_f32_kernel(const GemmParams P) {
+  __shared__ float As[2][BK][TBM + PAD];
   __shared__ float Bs[2][BK][BN + PAD];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int kl = lane >> 5, ml = lane & 31;
-  const int64_t m0 = int64_t(blockIdx.x) * BM;
-  const int64_t n0 = int64_t(blockIdx.y) * (MODE == kPlain ? BN : BN / 2);
+  const uint32_t tile = xcd_contiguous(blockIdx.x, gridDim.x);
+  const int64_t m0 = int64_t(tile / uint32_t(P.tiles_n)) * TBM;
+  const int64_t n0 = int64_t(tile % uint32_t(P.tiles_n)) * (MODE == kPlain ? BN : BN / 2);
   const int64_t k_begin = int64_t(blockIdx.z) * P.k_split;
   const int64_t k_end = (k_begin + P.k_split < P.K) ? k_begin + P.k_split : P.K;
   floatx16 acc[2][2];
-  tile_mainloop<MODE>(P, m0, P.M - m0, n0, k_begin, k_end, As, Bs, acc);
+  tile_mainloop<MODE, TBM>(P, m0, P.M - m0, n0, k_begin, k_end, As, Bs, acc);
 
   // Epilogue.
 #pragma unroll
@@ -154,20 +158,30 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, bool step) {
 
 namespace {
 
-sr_status launch_mode(int mode, GemmParams P, int64_t tiles_m, int64_t tiles_n, float* ws,
-                      hipStream_t stream) {
-  const int S = gemm_splits(P.M, P.ncols, P.K, mode == kStep);
+sr_status launch_mode(int mode, GemmParams P, float* ws, hipStream_t stream) {
+  const int64_t cols_per_tile = mode == kPlain ? BN : BN / 2;
+  const int64_t n_cols = mode == kPlain ? P.N : P.D_h;
+  P.tiles_n = (n_cols + cols_per_tile - 1) / cols_per_tile;
+  // Large plain products (enough 256-row tiles to fill the part twice over)
+  // use 256-row tiles and no K split; the rest 128-row tiles, splitting K
+  // when there are too few tiles.
+  const int64_t tiles_256 = ((P.M + 255) / 256) * P.tiles_n;
+  const bool big = mode == kPlain && tiles_256 >= 512;
+  const int tbm = big ? 256 : BM;
+  const int S = big ? 1 : gemm_splits(P.M, P.ncols, P.K, mode == kStep);
   P.k_split = S > 1 ? ((P.K + S - 1) / S + BK - 1) / BK * BK : (P.K > 0 ? P.K : 1);
   P.partial = S > 1 ? ws : nullptr;
   if (S > 1 && ws == nullptr) return fail(SR_ERR_INVALID_ARGUMENT, "GEMM split-K workspace missing");
-  if (tiles_m > 0x7FFFFFFF || tiles_n > 65535)
-    return fail(SR_ERR_UNSUPPORTED, "GEMM grid %lld x %lld too large", (long long)tiles_m,
-                (long long)tiles_n);
-  const dim3 grid{uint32_t(tiles_m), uint32_t(tiles_n), uint32_t(S)};
-  if (mode == kPlain)
-    hipLaunchKernelGGL(gemm_f32_kernel<kPlain>, grid, dim3(256), 0, stream, P);
+  const int64_t tiles = ((P.M + tbm - 1) / tbm) * P.tiles_n;
+  if (tiles > 0x7FFFFFFF / (2 * tbm))
+    return fail(SR_ERR_UNSUPPORTED, "GEMM of %lld tiles too large", (long long)tiles);
+  const dim3 grid{uint32_t(tiles), 1, uint32_t(S)};
+  if (mode == kPlain && big)
+    hipLaunchKernelGGL((gemm_f32_kernel<kPlain, 256>), grid, dim3(512), 0, stream, P);
+  else if (mode == kPlain)
+    hipLaunchKernelGGL((gemm_f32_kernel<kPlain, BM>), grid, dim3(2 * BM), 0, stream, P);
   else
-    hipLaunchKernelGGL(gemm_f32_kernel<kStep>, grid, dim3(256), 0, stream, P);
+    hipLaunchKernelGGL((gemm_f32_kernel<kStep, BM>), grid, dim3(2 * BM), 0, stream, P);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return fail(SR_ERR_HIP, "GEMM launch: %s", hipGetErrorString(err));
   if (S > 1) {
@@ -194,7 +208,7 @@ sr_status launch_gemm_f32(int64_t M, int64_t N, int64_t K, const float* A, int64
   P.M = M; P.N = N; P.K = K;
   P.A = A; P.lda = lda; P.Bm = Bm; P.ldb = ldb; P.C = C; P.ldc = ldc;
   P.ncols = N;
-  return launch_mode(kPlain, P, (M + BM - 1) / BM, (N + BN - 1) / BN, ws, stream);
+  return launch_mode(kPlain, P, ws, stream);
 }
 
 sr_status launch_step_in(int64_t Bsz, int64_t D_in, int64_t D_h, const float* x_t,
@@ -212,7 +226,7 @@ sr_status launch_step_in(int64_t Bsz, int64_t D_in, int64_t D_h, const float* x_
     P.saturated = decay->saturated;
   }
   P.ncols = 2 * D_h;
-  return launch_mode(kStep, P, (Bsz + BM - 1) / BM, (D_h + BN / 2 - 1) / (BN / 2), ws, stream);
+  return launch_mode(kStep, P, ws, stream);
 }
 
 }  // namespace sr

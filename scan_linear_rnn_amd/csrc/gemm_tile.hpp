@@ -1,10 +1,11 @@
 // One 128 x 128 fp32 MFMA tile and its K loop, shared by the plain / step
 // GEMM kernels (gemm.hip) and the fused projection + scan (fused.hip).
 //
-// Tiling: a 256-thread workgroup computes a 128 x 128 tile of C; its four
-// waves each own 64 x 64 (2 x 2 MFMA tiles of 32 x 32, 64 accumulators per
-// lane).  K advances 16 at a time through double-buffered LDS tiles; global
-// loads for step k+1 are in flight while the matrix cores work on step k.
+// Tiling: a workgroup computes a TBM x 128 tile of C (TBM = 128 with 4
+// waves, or 256 with 8 waves); each wave owns 64 x 64 (2 x 2 MFMA tiles of
+// 32 x 32, 64 accumulators per lane).  K advances 16 at a time through
+// double-buffered LDS tiles; global loads for step k+1 are in flight while
+// the matrix cores work on step k.
 //
 // Operand layout of v_mfma_f32_32x32x2_f32 (one 32x32x2 product per wave):
 // lane l supplies A[l % 32][l / 32] and B[l / 32][l % 32]; accumulator r of
@@ -50,6 +51,7 @@ struct GemmParams {
   int64_t k_split;
   float* partial;
   int64_t ncols;
+  int64_t tiles_n;  // tiles along N (blockIdx.x = m_tile * tiles_n + n_tile)
 };
 
 // Global column of B (and C) for block column c of the tile starting at n0.
@@ -68,29 +70,35 @@ __device__ __forceinline__ bool b_col_ok(const GemmParams& P, int64_t n0, int c)
   return n0 + 32 * wn + j < P.D_h;
 }
 
-// The K loop of one tile: A rows row0 .. row0 + rows - 1 (rows <= BM; the
-// rest of the tile reads zeros), B columns from n0 (MODE decides how), K in
-// [k_begin, k_end).  Leaves the sums in acc and ends with a barrier, after
-// which As / Bs are free.
-template <int MODE>
+// The K loop of one tile of TBM (128 or 256) rows x BN columns, run by
+// 2 * TBM threads: TBM / 64 x 2 waves, each owning 64 x 64 (2 x 2 MFMA tiles
+// of 32 x 32).  A rows row0 .. row0 + rows - 1 (the rest of the tile reads
+// zeros), B columns from n0 (MODE decides how), K in [k_begin, k_end).
+// Leaves the sums in acc and ends with a barrier, after which As / Bs are
+// free.
+template <int MODE, int TBM>
 __device__ __forceinline__ void tile_mainloop(const GemmParams& P, int64_t row0, int64_t rows,
                                               int64_t n0, int64_t k_begin, int64_t k_end,
-                                              float (&As)[2][BK][BM + PAD],
+                                              float (&As)[2][BK][TBM + PAD],
                                               float (&Bs)[2][BK][BN + PAD],
                                               floatx16 (&acc)[2][2]) {
+  static_assert(TBM == 128 || TBM == 256, "tile rows");
+  constexpr int NTH = 2 * TBM;
+  constexpr int BPER = BK * BN / NTH;      // B floats per thread: 8 or 4
+  constexpr int BTPR = BN / BPER;          // threads per B row
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  // Global -> register staging: A tile 128 x 16 (8 floats per thread, one row),
-  // B tile 16 x 128 (8 floats per thread, one k row).
+  // Global -> register staging: A tile TBM x 16 (8 floats per thread, one
+  // row), B tile 16 x 128 (BPER floats per thread, one k row).
   const int a_row = tid >> 1, a_k = (tid & 1) * 8;
-  const int b_k = tid >> 4, b_c = (tid & 15) * 8;
+  const int b_k = tid / BTPR, b_c = (tid % BTPR) * BPER;
   const bool a_vec = (P.lda % 4 == 0) && ((reinterpret_cast<uintptr_t>(P.A) & 15) == 0);
   const bool b_vec = (P.ldb % 4 == 0) && ((reinterpret_cast<uintptr_t>(P.Bm) & 15) == 0) &&
                      (MODE == kPlain || P.D_h % 4 == 0);
-  float ra[8], rb[8];
+  float ra[8], rb[BPER];
 
   auto load_tiles = [&](int64_t k0) {
     const bool row_ok = a_row < rows;
@@ -108,14 +116,16 @@ __device__ __forceinline__ void tile_mainloop(const GemmParams& P, int64_t row0,
     }
     const int64_t bk = k0 + b_k;
     const int64_t gc = b_col<MODE>(P, n0, b_c);
-    if (bk < k_end && b_vec && b_col_ok<MODE>(P, n0, b_c + 7)) {
+    if (bk < k_end && b_vec && b_col_ok<MODE>(P, n0, b_c + BPER - 1)) {
       const float4* src = reinterpret_cast<const float4*>(P.Bm + bk * P.ldb + gc);
-      const float4 u = src[0], v = src[1];
-      rb[0] = u.x; rb[1] = u.y; rb[2] = u.z; rb[3] = u.w;
-      rb[4] = v.x; rb[5] = v.y; rb[6] = v.z; rb[7] = v.w;
+#pragma unroll
+      for (int v = 0; v < BPER / 4; ++v) {
+        const float4 u = src[v];
+        rb[4 * v + 0] = u.x; rb[4 * v + 1] = u.y; rb[4 * v + 2] = u.z; rb[4 * v + 3] = u.w;
+      }
     } else {
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
+      for (int j = 0; j < BPER; ++j)
         rb[j] = (bk < k_end && b_col_ok<MODE>(P, n0, b_c + j))
                     ? P.Bm[bk * P.ldb + b_col<MODE>(P, n0, b_c + j)]
                     : 0.0f;
@@ -125,7 +135,7 @@ __device__ __forceinline__ void tile_mainloop(const GemmParams& P, int64_t row0,
 #pragma unroll
     for (int j = 0; j < 8; ++j) As[buf][a_k + j][a_row] = ra[j];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) Bs[buf][b_k][b_c + j] = rb[j];
+    for (int j = 0; j < BPER; ++j) Bs[buf][b_k][b_c + j] = rb[j];
   };
 
 #pragma unroll
@@ -156,11 +166,17 @@ __device__ __forceinline__ void tile_mainloop(const GemmParams& P, int64_t row0,
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < n_k) {
-      store_tiles(buf ^ 1);
-    }
+    if (kt + 1 < n_k) store_tiles(buf ^ 1);
     __syncthreads();
   }
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own
+// L2).  Renumbering so that each XCD gets a contiguous range of tile ids
+// keeps tiles that share operands on one L2.
+__device__ __forceinline__ uint32_t xcd_contiguous(uint32_t bid, uint32_t n) {
+  const uint32_t per = n / 8;
+  return bid < per * 8 ? (bid % 8) * per + bid / 8 : bid;
 }
 
 }  // namespace gt

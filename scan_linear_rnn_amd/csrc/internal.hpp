@@ -65,7 +65,7 @@ ScanGeometry choose_geometry(const ScanRequest& rq);
 // Fused input projection + scan (fused.hip): h = scan(x W_in), the [k|p]
 // tile never leaving the workgroup.  Used for large enough problems (see
 // fused_forward_applies); its workspace is the look-back words of its own
-// 128-step tiles.
+// 256-step tiles.
 struct FusedRequest {
   int64_t B, T, D_in, D_h;
   const float* x;      // [B,T,D_in]

@@ -49,7 +49,7 @@ def test_workspace_sizes():
     s2 = lib.mingru_forward_workspace_size(8, 65536, 1024, 1024, 1024, 1, 1)
     assert 0 < s0 < 2 ** 27
     assert 0 < s1 < 2 ** 27
-    assert s1 >= 256 + 512 * 8 * 1024 * 8          # ceil(65536 / 128) tiles of words
+    assert s1 >= 256 + 256 * 8 * 1024 * 8          # ceil(65536 / 256) tiles of words
     assert s2 - s1 >= 8 * 65536 * 1024 * 4
     small = lib.mingru_forward_workspace_size(2, 1024, 512, 512, 512, 1, 0)   # 128 tiles: staged
     assert small >= 2 * 1024 * 1024 * 4

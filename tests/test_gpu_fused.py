@@ -1,5 +1,5 @@
 """GPU parity of the fused projection + scan (taken by mingru_forward with W_in
-when the problem has at least 1024 tiles of 128 steps x 64 channels)."""
+when the problem has at least 512 tiles of 256 steps x 64 channels)."""
 
 import numpy as np
 import pytest
@@ -33,8 +33,9 @@ def _case(B, T, D_in, D_h, D_out, seed):
 @pytest.mark.parametrize("B,T,D_in,D_h,D_out,with_out,with_h0", [
     (8, 1000, 64, 1024, 1024, True, True),     # ragged last tile along T
     (10, 777, 40, 1000, 1000, False, False),   # ragged along T and D, K not a multiple of 16
+    (2, 4100, 16, 2048, 2048, False, True),    # a 4-step last tile
     (4, 2048, 96, 2048, 512, True, False),
-    (1, 16384, 32, 512, 512, False, True),     # one batch row, 128 tiles along T
+    (1, 16384, 32, 512, 512, False, True),     # one batch row, 64 tiles along T
 ])
 def test_fused_forward_matches_oracle(B, T, D_in, D_h, D_out, with_out, with_h0):
     say(f"fused B={B} T={T} D_in={D_in} D_h={D_h} D_out={D_out} out={with_out} h0={with_h0}")
