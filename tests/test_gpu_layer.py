@@ -161,3 +161,23 @@ def test_decode_config_4():
     e = np.max(np.abs(h[rows].double().cpu().numpy() - ref) / np.abs(ref))
     say("decode final err", e)
     assert e < TOL_F32
+
+
+@pytest.mark.parametrize("B,T,D_h,D_out", [
+    (4, 8192, 256, 1024),     # 128 x 8 tiles of 256 x 128: the large-product path
+    (3, 5000, 200, 1100),     # ragged rows, columns and K
+])
+def test_large_output_projection(B, T, D_h, D_out):
+    """y = h W_out on a product large enough for the 256-row tiles, from a
+    scan-only forward (k, p given)."""
+    say(f"large W_out B={B} T={T} D_h={D_h} D_out={D_out}")
+    rng = np.random.default_rng([1400, B, T])
+    k = rng.normal(-1.0, 1.0, (B, T, D_h)).astype(np.float32)
+    p = rng.standard_normal((B, T, D_h)).astype(np.float32)
+    W_out = (rng.standard_normal((D_h, D_out)) / D_h ** 0.5).astype(np.float32)
+    y = sr.mingru_forward(k=dev(k), p=dev(p), W_out=dev(W_out))
+    h_ref = mingru.scan(k, p)
+    y_ref = mingru.project(h_ref, W_out)
+    err = metrics.y_rel_err(y.double().cpu().numpy(), y_ref, h_ref, W_out)
+    say("error", err)
+    assert err < TOL_F32
