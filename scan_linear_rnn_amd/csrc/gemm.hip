@@ -106,6 +106,62 @@ __global__ __launch_bounds__(2 * TBM) void gemm_f32_kernel(const GemmParams P) {
   }
 }
 
+// Products with at most kSmallM rows (a step over a few streams): a
+// 128-row MFMA tile would spend its whole K loop on them, so they run on
+// fp32 FMAs instead.  A workgroup of 1024 threads owns 64 columns (step
+// mode: 32 channels, k then p) and all rows; thread (c, s) accumulates
+// column c over the s-th of 16 K slices, and the slices are summed in LDS
+// in slice order (deterministic), then stored or used by the step update.
+constexpr int kSmallM = 16;
+constexpr int kSmallSlices = 16;
+
+template <int MODE, int MR>
+__global__ __launch_bounds__(64 * kSmallSlices) void small_m_kernel(const GemmParams P) {
+  __shared__ float red[kSmallSlices][MR][64];
+  const int c = threadIdx.x & 63, sl = threadIdx.x >> 6;
+  int64_t col;
+  bool col_ok;
+  if (MODE == kPlain) {
+    col = int64_t(blockIdx.x) * 64 + c;
+    col_ok = col < P.N;
+  } else {
+    const int64_t ch = int64_t(blockIdx.x) * 32 + (c & 31);
+    col = (c < 32 ? 0 : P.D_h) + ch;
+    col_ok = ch < P.D_h;
+  }
+  const int64_t ks = (P.K + kSmallSlices - 1) / kSmallSlices;
+  const int64_t k0 = sl * ks, k1 = (k0 + ks < P.K) ? k0 + ks : P.K;
+  float acc[MR];
+#pragma unroll
+  for (int m = 0; m < MR; ++m) acc[m] = 0.0f;
+  if (col_ok) {
+    for (int64_t k = k0; k < k1; ++k) {
+      const float b = P.Bm[k * P.ldb + col];
+#pragma unroll
+      for (int m = 0; m < MR; ++m)
+        if (m < P.M) acc[m] = fmaf(P.A[m * P.lda + k], b, acc[m]);
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < MR; ++m) red[sl][m][c] = acc[m];
+  __syncthreads();
+  // Thread (c, m): the slices of (row m, column c), in order.
+  const int m = threadIdx.x >> 6;
+  if (m < MR && m < P.M) {
+    float v = 0.0f;
+#pragma unroll
+    for (int q = 0; q < kSmallSlices; ++q) v += red[q][m][c];
+    if (MODE == kPlain) {
+      if (col_ok) P.C[m * P.ldc + col] = v;
+    } else if (c < 32 && col_ok) {
+      float vp = 0.0f;
+#pragma unroll
+      for (int q = 0; q < kSmallSlices; ++q) vp += red[q][m][c + 32];
+      step_update(P, m, int64_t(blockIdx.x) * 32 + c, v, vp);
+    }
+  }
+}
+
 // Split-K reductions: the K slices' sums are added in slice order (so the
 // result does not depend on scheduling), then stored or used by the step.
 __global__ void reduce_plain_kernel(const float* part, int S, int64_t M, int64_t N, float* C,
@@ -137,7 +193,9 @@ __global__ void reduce_step_kernel(const GemmParams P, int S) {
 int gemm_splits(int64_t M, int64_t N, int64_t K, bool step) {
   // Enough workgroups for two per CU on a 256-CU part, each K slice at
   // least 256 deep; small problems (the single-token step) split K, large
-  // ones (whole-sequence projections) do not.
+  // ones (whole-sequence projections) do not.  Products of at most kSmallM
+  // rows take the FMA path, which splits K inside the workgroup.
+  if (M <= kSmallM) return 1;
   const int64_t tiles = ((M + BM - 1) / BM) * (step ? (N / 2 + BN / 2 - 1) / (BN / 2)
                                                     : (N + BN - 1) / BN);
   if (tiles <= 0 || tiles >= 512) return 1;
@@ -158,7 +216,30 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, bool step) {
 
 namespace {
 
+template <int MODE>
+hipError_t launch_small_m(const GemmParams& P, hipStream_t stream) {
+  const int64_t blocks = MODE == kPlain ? (P.N + 63) / 64 : (P.D_h + 31) / 32;
+  const dim3 grid{uint32_t(blocks)}, block{64 * kSmallSlices};
+  if (P.M <= 2)
+    hipLaunchKernelGGL((small_m_kernel<MODE, 2>), grid, block, 0, stream, P);
+  else if (P.M <= 4)
+    hipLaunchKernelGGL((small_m_kernel<MODE, 4>), grid, block, 0, stream, P);
+  else if (P.M <= 8)
+    hipLaunchKernelGGL((small_m_kernel<MODE, 8>), grid, block, 0, stream, P);
+  else
+    hipLaunchKernelGGL((small_m_kernel<MODE, kSmallM>), grid, block, 0, stream, P);
+  return hipGetLastError();
+}
+
 sr_status launch_mode(int mode, GemmParams P, float* ws, hipStream_t stream) {
+  if (P.M <= kSmallM) {
+    if (P.M > 0 && (mode == kPlain ? P.N : P.D_h) > int64_t(0x7FFFFFFF) * 32)
+      return fail(SR_ERR_UNSUPPORTED, "GEMM too wide");
+    const hipError_t e = mode == kPlain ? launch_small_m<kPlain>(P, stream)
+                                        : launch_small_m<kStep>(P, stream);
+    if (e != hipSuccess) return fail(SR_ERR_HIP, "small GEMM launch: %s", hipGetErrorString(e));
+    return SR_OK;
+  }
   const int64_t cols_per_tile = mode == kPlain ? BN : BN / 2;
   const int64_t n_cols = mode == kPlain ? P.N : P.D_h;
   P.tiles_n = (n_cols + cols_per_tile - 1) / cols_per_tile;

@@ -181,3 +181,23 @@ def test_large_output_projection(B, T, D_h, D_out):
     err = metrics.y_rel_err(y.double().cpu().numpy(), y_ref, h_ref, W_out)
     say("error", err)
     assert err < TOL_F32
+
+
+@pytest.mark.parametrize("B", [1, 5, 16, 17, 40])
+def test_step_batch_sizes(B):
+    """The step's products run on FMAs up to 16 streams and on the matrix
+    cores above; both against the fp64 oracle, three steps carried."""
+    say(f"step B={B}")
+    rng = np.random.default_rng([1500, B])
+    D_in, D_h, D_out = 96, 160, 80
+    W_in = (rng.standard_normal((D_in, 2 * D_h)) / D_in ** 0.5).astype(np.float32)
+    W_out = (rng.standard_normal((D_h, D_out)) / D_h ** 0.5).astype(np.float32)
+    h = dev(rng.standard_normal((B, D_h)).astype(np.float32))
+    h_ref = host64(h)
+    for t in range(3):
+        x_t = rng.standard_normal((B, D_in)).astype(np.float32)
+        y_t, h = sr.mingru_step(dev(x_t), dev(W_in), dev(W_out), h_prev=h)
+        y_ref, h_ref = mingru.step(x_t, W_in, W_out, h_ref)
+        assert metrics.max_abs_rel(host64(h), h_ref) < TOL_F32
+        assert metrics.y_rel_err(host64(y_t), y_ref, h_ref, W_out) < TOL_F32
+        h_ref = host64(h)
