@@ -55,7 +55,7 @@ __device__ __forceinline__ void step_update(const GemmParams& P, int64_t row, in
 // One TBM x 128 tile per workgroup; blockIdx.x numbers the tiles (N tiles
 // fastest, so consecutive tiles share their A rows; renumbered per XCD),
 // blockIdx.z the K slice.
-template <int MODE, int TBM>
+template <int MODE, int TBM, bool FULL>
 __global__ __launch_bounds__(2 * TBM) void gemm_f32_kernel(const GemmParams P) {
   __shared__ float As[2][BK][TBM + PAD];
   __shared__ float Bs[2][BK][BN + PAD];
@@ -70,7 +70,7 @@ __global__ __launch_bounds__(2 * TBM) void gemm_f32_kernel(const GemmParams P) {
   const int64_t k_begin = int64_t(blockIdx.z) * P.k_split;
   const int64_t k_end = (k_begin + P.k_split < P.K) ? k_begin + P.k_split : P.K;
   floatx16 acc[2][2];
-  tile_mainloop<MODE, TBM>(P, m0, P.M - m0, n0, k_begin, k_end, As, Bs, acc);
+  tile_mainloop<MODE, TBM, FULL>(P, m0, P.M - m0, n0, k_begin, k_end, As, Bs, acc);
 
   // Epilogue.
 #pragma unroll
@@ -231,6 +231,14 @@ hipError_t launch_small_m(const GemmParams& P, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int MODE, int TBM>
+void launch_tiles(bool full, dim3 grid, const GemmParams& P, hipStream_t stream) {
+  if (full)
+    hipLaunchKernelGGL((gemm_f32_kernel<MODE, TBM, true>), grid, dim3(2 * TBM), 0, stream, P);
+  else
+    hipLaunchKernelGGL((gemm_f32_kernel<MODE, TBM, false>), grid, dim3(2 * TBM), 0, stream, P);
+}
+
 sr_status launch_mode(int mode, GemmParams P, float* ws, hipStream_t stream) {
   if (P.M <= kSmallM) {
     if (P.M > 0 && (mode == kPlain ? P.N : P.D_h) > int64_t(0x7FFFFFFF) * 32)
@@ -257,12 +265,18 @@ sr_status launch_mode(int mode, GemmParams P, float* ws, hipStream_t stream) {
   if (tiles > 0x7FFFFFFF / (2 * tbm))
     return fail(SR_ERR_UNSUPPORTED, "GEMM of %lld tiles too large", (long long)tiles);
   const dim3 grid{uint32_t(tiles), 1, uint32_t(S)};
+  // Every tile full (rows, columns, whole K steps in every slice) and
+  // 16-byte operands: the loads need no range tests.
+  const auto al16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
+  const bool full = P.M % tbm == 0 && n_cols % cols_per_tile == 0 && P.K % BK == 0 &&
+                    P.k_split % BK == 0 && P.K % P.k_split == 0 && P.lda % 4 == 0 &&
+                    P.ldb % 4 == 0 && al16(P.A) && al16(P.Bm) && (mode == kPlain || P.D_h % 4 == 0);
   if (mode == kPlain && big)
-    hipLaunchKernelGGL((gemm_f32_kernel<kPlain, 256>), grid, dim3(512), 0, stream, P);
+    launch_tiles<kPlain, 256>(full, grid, P, stream);
   else if (mode == kPlain)
-    hipLaunchKernelGGL((gemm_f32_kernel<kPlain, BM>), grid, dim3(2 * BM), 0, stream, P);
+    launch_tiles<kPlain, BM>(full, grid, P, stream);
   else
-    hipLaunchKernelGGL((gemm_f32_kernel<kStep, BM>), grid, dim3(2 * BM), 0, stream, P);
+    launch_tiles<kStep, BM>(full, grid, P, stream);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return fail(SR_ERR_HIP, "GEMM launch: %s", hipGetErrorString(err));
   if (S > 1) {

@@ -75,8 +75,10 @@ __device__ __forceinline__ bool b_col_ok(const GemmParams& P, int64_t n0, int c)
 // of 32 x 32).  A rows row0 .. row0 + rows - 1 (the rest of the tile reads
 // zeros), B columns from n0 (MODE decides how), K in [k_begin, k_end).
 // Leaves the sums in acc and ends with a barrier, after which As / Bs are
-// free.
-template <int MODE, int TBM>
+// free.  FULL: the host has checked that every row, column and K step of
+// the tile is in range and the operands allow 16-byte loads, so the loads
+// need no tests and walk two pointers.
+template <int MODE, int TBM, bool FULL = false>
 __device__ __forceinline__ void tile_mainloop(const GemmParams& P, int64_t row0, int64_t rows,
                                               int64_t n0, int64_t k_begin, int64_t k_end,
                                               float (&As)[2][BK][TBM + PAD],
@@ -99,7 +101,23 @@ __device__ __forceinline__ void tile_mainloop(const GemmParams& P, int64_t row0,
   const bool b_vec = (P.ldb % 4 == 0) && ((reinterpret_cast<uintptr_t>(P.Bm) & 15) == 0) &&
                      (MODE == kPlain || P.D_h % 4 == 0);
   float ra[8], rb[BPER];
+  const float* a_ptr = P.A + (row0 + a_row) * P.lda + k_begin + a_k;
+  const float* b_ptr = P.Bm + (k_begin + b_k) * P.ldb + b_col<MODE>(P, n0, b_c);
 
+  auto load_full = [&]() {
+    const float4* sa = reinterpret_cast<const float4*>(a_ptr);
+    const float4 u = sa[0], v = sa[1];
+    ra[0] = u.x; ra[1] = u.y; ra[2] = u.z; ra[3] = u.w;
+    ra[4] = v.x; ra[5] = v.y; ra[6] = v.z; ra[7] = v.w;
+    const float4* sb = reinterpret_cast<const float4*>(b_ptr);
+#pragma unroll
+    for (int q = 0; q < BPER / 4; ++q) {
+      const float4 w = sb[q];
+      rb[4 * q + 0] = w.x; rb[4 * q + 1] = w.y; rb[4 * q + 2] = w.z; rb[4 * q + 3] = w.w;
+    }
+    a_ptr += BK;
+    b_ptr += BK * P.ldb;
+  };
   auto load_tiles = [&](int64_t k0) {
     const bool row_ok = a_row < rows;
     const int64_t gm = row0 + a_row;
@@ -145,14 +163,16 @@ __device__ __forceinline__ void tile_mainloop(const GemmParams& P, int64_t row0,
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int64_t n_k = k_end > k_begin ? (k_end - k_begin + BK - 1) / BK : 0;
-  load_tiles(k_begin);
+  const int n_k = k_end > k_begin ? int((k_end - k_begin + BK - 1) / BK) : 0;
+  if constexpr (FULL) load_full(); else load_tiles(k_begin);
   store_tiles(0);
   __syncthreads();
   const int kl = lane >> 5, ml = lane & 31;
-  for (int64_t kt = 0; kt < n_k; ++kt) {
-    const int buf = int(kt & 1);
-    if (kt + 1 < n_k) load_tiles(k_begin + (kt + 1) * BK);
+  for (int kt = 0; kt < n_k; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < n_k) {
+      if constexpr (FULL) load_full(); else load_tiles(k_begin + int64_t(kt + 1) * BK);
+    }
 #pragma unroll
     for (int kk = 0; kk < BK / 2; ++kk) {
       float a[2], b[2];
