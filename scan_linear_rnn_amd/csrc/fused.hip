@@ -46,7 +46,7 @@ struct FusedParams {
 // 256-row GEMM runs.  The scan epilogue then spills a few dozen registers,
 // once per tile; measured 17.3 ms against 19.1 ms at the compiler's own
 // choice (2 waves per SIMD) on the config-4 prefill projection.
-template <bool kDecay>
+template <bool kDecay, bool kFull>
 __global__ __launch_bounds__(2 * kTileT) __attribute__((amdgpu_waves_per_eu(4)))
 void fused_proj_scan_kernel(const FusedParams F) {
   __shared__ float As[2][BK][kTileT + PAD];
@@ -83,7 +83,7 @@ void fused_proj_scan_kernel(const FusedParams F) {
   }
 
   floatx16 acc[2][2];
-  tile_mainloop<kStep, kTileT>(F.g, tl.b * P.T + t0, rows, tl.d0, 0, F.g.K, As, Bs, acc);
+  tile_mainloop<kStep, kTileT, kFull>(F.g, tl.b * P.T + t0, rows, tl.d0, 0, F.g.K, As, Bs, acc);
 
   // 1. Maps in place of the sums (set 0 <- coefficient, set 1 <- offset);
   // rows past T become the identity.  Then the runs of 4 rows: run n = (i, q),
@@ -206,12 +206,20 @@ sr_status launch_fused_forward(const FusedRequest& rq) {
   const size_t used = eng::kHeaderBytes + size_t(P.n_tchunks) * size_t(rq.B) * size_t(rq.D_h) * 8;
   sr_status st = eng::reset_workspace(ws, used, rq.stream);
   if (st != SR_OK) return st;
-  if (rq.decay_rate != nullptr)
-    hipLaunchKernelGGL(fused_proj_scan_kernel<true>, dim3(uint32_t(tiles)), dim3(2 * kTileT), 0,
-                       rq.stream, F);
+  // Every tile full (whole 256-step tiles, whole channel tiles, K in steps
+  // of 16) with 16-byte operands: the K loop needs no range tests.
+  const auto al16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
+  const bool full = rq.T % kTileT == 0 && rq.D_h % kTileD == 0 && rq.D_in % BK == 0 &&
+                    rq.D_in % 4 == 0 && al16(rq.x) && al16(rq.W_in);
+  const dim3 grid{uint32_t(tiles)}, block{2 * kTileT};
+  if (rq.decay_rate != nullptr && full)
+    hipLaunchKernelGGL((fused_proj_scan_kernel<true, true>), grid, block, 0, rq.stream, F);
+  else if (rq.decay_rate != nullptr)
+    hipLaunchKernelGGL((fused_proj_scan_kernel<true, false>), grid, block, 0, rq.stream, F);
+  else if (full)
+    hipLaunchKernelGGL((fused_proj_scan_kernel<false, true>), grid, block, 0, rq.stream, F);
   else
-    hipLaunchKernelGGL(fused_proj_scan_kernel<false>, dim3(uint32_t(tiles)), dim3(2 * kTileT), 0,
-                       rq.stream, F);
+    hipLaunchKernelGGL((fused_proj_scan_kernel<false, false>), grid, block, 0, rq.stream, F);
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return fail(SR_ERR_HIP, "fused projection + scan launch: %s", hipGetErrorString(err));
   return SR_OK;
