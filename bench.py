@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the gfx950 minGRU log-space scan (and its sibling paths).
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs c3,c5,c4,c2,c1]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs scan,minmax,decode,...]
 
 One step is one pass of the scan hot path over one batch: the headline
 workload is the long-sequence scan B=8, T=65536, D=1024 with bf16 gate logits
@@ -19,9 +19,12 @@ carries:
                 ``traffic`` comes from committed rocprofv3 counter runs when
                 they were taken on the current kernel source, else null;
 * cpu_baseline -- the fp64 CPU oracle timed on a bounded sample of the same
-                workload (every channel, a prefix of the sequence);
-* legs       -- the other measurements: the MinMax scan, the decode-style
-                step loop, the small layers, and a device copy ceiling.
+                workload (every channel; by default the whole sequence,
+                --cpu-steps takes a prefix);
+* legs       -- the other measurements: the MinMax scan, the backward passes
+                of both scans, the time-decayed scan, the decode-style step
+                loop with its prefill, the small layers, and a device copy
+                ceiling.
 
 Only one GPU is used; --gpus above 1 exits with a message.
 """
@@ -75,11 +78,11 @@ def time_launches(torch, fn, steps, warmup):
     return wall, sum(per) / len(per), min(per)
 
 
-def leg_c3(torch, sr, synth, steps, warmup, cpu_steps):
+def leg_scan(torch, sr, synth, steps, warmup, cpu_steps):
     import ctypes
     cfg = synth.CONFIGS[3]
     B, T, D = cfg["B"], cfg["T"], cfg["D"]
-    log(f"[bench] c3 scan B={B} T={T} D={D}: generating inputs")
+    log(f"[bench] scan B={B} T={T} D={D}: generating inputs")
     kb = synth.device_normal(3, "k", (B, T, D), cfg["k_mean"], cfg["k_std"], torch.bfloat16)
     pb = synth.device_normal(3, "p", (B, T, D), cfg["p_mean"], cfg["p_std"], torch.bfloat16)
     h0 = synth.device_normal(3, "h0", (B, D))
@@ -99,7 +102,7 @@ def leg_c3(torch, sr, synth, steps, warmup, cpu_steps):
         if st:
             raise RuntimeError(lib.scanrnn_last_error().decode())
 
-    log(f"[bench] c3: {warmup} warmup + {steps} timed steps")
+    log(f"[bench] scan: {warmup} warmup + {steps} timed steps")
     wall, mean_ms, min_ms = time_launches(torch, step, steps, warmup)
     if sr.workspace_status(ws) != 0:
         raise RuntimeError("look-back wait expired during the benchmark")
@@ -124,7 +127,7 @@ def leg_c3(torch, sr, synth, steps, warmup, cpu_steps):
                   "kernel": "chunk_scan_kernel<MinGRUOp, bf16, V=2> (+ workspace reset)"},
     )
     if cpu_steps > 0:
-        log(f"[bench] c3: CPU oracle on every channel, first {cpu_steps} steps")
+        log(f"[bench] scan: CPU oracle on every channel, first {cpu_steps} steps")
         from oracle import mingru
         ks = kb[:, :cpu_steps].double().cpu().numpy()
         ps = pb[:, :cpu_steps].double().cpu().numpy()
@@ -143,10 +146,10 @@ def leg_c3(torch, sr, synth, steps, warmup, cpu_steps):
     return res
 
 
-def leg_c5(torch, sr, synth, steps, warmup):
+def leg_minmax(torch, sr, synth, steps, warmup):
     cfg = synth.CONFIGS[5]
     B, T, D = cfg["B"], cfg["T"], cfg["D"]
-    log(f"[bench] c5 minmax B={B} T={T} D={D}")
+    log(f"[bench] minmax B={B} T={T} D={D}")
     r = synth.device_uniform(5, "r", (B, T, D), -1.0, 1.0)
     s = synth.device_uniform(5, "s", (B, T, D), -1.5, 0.5)
     x0 = synth.device_uniform(5, "x0", (B, D), -1.0, 1.0)
@@ -166,12 +169,12 @@ def leg_c5(torch, sr, synth, steps, warmup):
                 frac_of_hbm_peak=alg / (mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS)
 
 
-def leg_c3_backward(torch, sr, synth, steps, warmup):
+def leg_scan_backward(torch, sr, synth, steps, warmup):
     """Backward of the headline scan: reads k, p (bf16), h, dh (fp32), writes
     dk, dp (fp32): 20 algorithmic bytes per element."""
     cfg = synth.CONFIGS[3]
     B, T, D = cfg["B"], cfg["T"], cfg["D"]
-    log(f"[bench] c3 backward B={B} T={T} D={D}")
+    log(f"[bench] scan backward B={B} T={T} D={D}")
     kb = synth.device_normal(3, "k", (B, T, D), cfg["k_mean"], cfg["k_std"], torch.bfloat16)
     pb = synth.device_normal(3, "p", (B, T, D), cfg["p_mean"], cfg["p_std"], torch.bfloat16)
     h0 = synth.device_normal(3, "h0", (B, D))
@@ -191,13 +194,13 @@ def leg_c3_backward(torch, sr, synth, steps, warmup):
     return res
 
 
-def leg_c3_decay(torch, sr, synth, steps, warmup):
+def leg_scan_decay(torch, sr, synth, steps, warmup):
     """The headline scan shape with time decay of the carried state: k, p
     (bf16) in, h (fp32) out as in the plain scan, plus one gap per (b, t) and
     one rate per channel: 8 + 4/D algorithmic bytes per element."""
     cfg = synth.CONFIGS[3]
     B, T, D = cfg["B"], cfg["T"], cfg["D"]
-    log(f"[bench] c3 decayed B={B} T={T} D={D}")
+    log(f"[bench] decayed scan B={B} T={T} D={D}")
     kb = synth.device_normal(3, "k", (B, T, D), cfg["k_mean"], cfg["k_std"], torch.bfloat16)
     pb = synth.device_normal(3, "p", (B, T, D), cfg["p_mean"], cfg["p_std"], torch.bfloat16)
     h0 = synth.device_normal(3, "h0", (B, D))
@@ -224,12 +227,12 @@ def leg_c3_decay(torch, sr, synth, steps, warmup):
     return res
 
 
-def leg_c5_backward(torch, sr, synth, steps, warmup):
+def leg_minmax_backward(torch, sr, synth, steps, warmup):
     """Backward of the MinMax scan: reads r, s, x_out, dx, writes dr, ds
     (fp32): 24 algorithmic bytes per element."""
     cfg = synth.CONFIGS[5]
     B, T, D = cfg["B"], cfg["T"], cfg["D"]
-    log(f"[bench] c5 backward B={B} T={T} D={D}")
+    log(f"[bench] minmax backward B={B} T={T} D={D}")
     r = synth.device_uniform(5, "r", (B, T, D), -1.0, 1.0)
     s = synth.device_uniform(5, "s", (B, T, D), -1.5, 0.5)
     x0 = synth.device_uniform(5, "x0", (B, D), -1.0, 1.0)
@@ -246,10 +249,10 @@ def leg_c5_backward(torch, sr, synth, steps, warmup):
                 frac_of_hbm_peak=alg / (mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS)
 
 
-def leg_c4(torch, sr, synth, n_steps):
+def leg_decode(torch, sr, synth, n_steps):
     cfg = synth.CONFIGS[4]
     B, D, Tp = cfg["B"], cfg["D"], cfg["T_prefill"]
-    log(f"[bench] c4 prefill B={B} T={Tp} D={D}, then {n_steps} steps")
+    log(f"[bench] decode: prefill B={B} T={Tp} D={D}, then {n_steps} steps")
     W_in = synth.device_normal(4, "W_in", (D, 2 * D), 0.0, cfg["w_std"])
     W_out = synth.device_normal(4, "W_out", (D, D), 0.0, cfg["w_std"])
     x = synth.device_normal(4, "x", (B, Tp + n_steps, D))
@@ -323,10 +326,10 @@ def main():
     # A fresh process reaches steady clocks only after a few hundred ms of
     # sustained load (measured: the first ~100 launches run 3-5% slower).
     ap.add_argument("--warmup", type=int, default=1000)
-    ap.add_argument("--legs", default="c3,c5,c3bwd,c5bwd,c3decay,c4,c2,c1,copy")
+    ap.add_argument("--legs", default="scan,minmax,scan_bwd,minmax_bwd,scan_decay,decode,layer_d512,layer_d16,copy")
     ap.add_argument("--cpu-steps", type=int, default=65536,
                     help="sequence prefix the CPU oracle baseline runs over (0 = skip)")
-    ap.add_argument("--c4-steps", type=int, default=4096)
+    ap.add_argument("--decode-steps", type=int, default=4096)
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -344,40 +347,40 @@ def main():
     legs = [s.strip() for s in args.legs.split(",") if s.strip()]
     out = {"metric": METRIC}
     extra = {}
-    c3 = None
-    if "c3" in legs:
-        c3 = leg_c3(torch, sr, synth, args.steps, args.warmup, args.cpu_steps)
+    head = None
+    if "scan" in legs:
+        head = leg_scan(torch, sr, synth, args.steps, args.warmup, args.cpu_steps)
     if "copy" in legs:
         extra["copy_ceiling"] = leg_copy(torch)
-    if "c5" in legs:
-        extra["minmax_b8_t32768_d192"] = leg_c5(torch, sr, synth, args.steps, args.warmup)
-    if "c3bwd" in legs:
-        extra["backward_b8_t65536_d1024"] = leg_c3_backward(torch, sr, synth, args.steps, args.warmup)
-    if "c5bwd" in legs:
-        extra["minmax_backward_b8_t32768_d192"] = leg_c5_backward(torch, sr, synth, args.steps,
+    if "minmax" in legs:
+        extra["minmax_b8_t32768_d192"] = leg_minmax(torch, sr, synth, args.steps, args.warmup)
+    if "scan_bwd" in legs:
+        extra["backward_b8_t65536_d1024"] = leg_scan_backward(torch, sr, synth, args.steps, args.warmup)
+    if "minmax_bwd" in legs:
+        extra["minmax_backward_b8_t32768_d192"] = leg_minmax_backward(torch, sr, synth, args.steps,
                                                                   args.warmup)
-    if "c3decay" in legs:
-        extra["decayed_b8_t65536_d1024"] = leg_c3_decay(torch, sr, synth, args.steps, args.warmup)
-    if "c2" in legs:
+    if "scan_decay" in legs:
+        extra["decayed_b8_t65536_d1024"] = leg_scan_decay(torch, sr, synth, args.steps, args.warmup)
+    if "layer_d512" in legs:
         extra["layer_b2_t1024_d512"] = leg_layer(torch, sr, synth, 2, 10)
-    if "c1" in legs:
+    if "layer_d16" in legs:
         extra["layer_b2_t64_d16"] = leg_layer(torch, sr, synth, 1, 10)
-    if "c4" in legs:
-        extra["step_b256_d2048"] = leg_c4(torch, sr, synth, args.c4_steps)
-    if c3 is not None:
+    if "decode" in legs:
+        extra["step_b256_d2048"] = leg_decode(torch, sr, synth, args.decode_steps)
+    if head is not None:
         out.update({
-            "value": c3["value"], "unit": "elements/s", "n_gpus": 1, "steps": args.steps,
-            "warmup": args.warmup, "ms_per_step": c3["ms_per_step"], "higher_is_better": True,
+            "value": head["value"], "unit": "elements/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
             "config": {"workload": "minGRU log-space scan, B=8 T=65536 D=1024, bf16 k/p inputs, "
-                                   "fp32 h0/h/h_T", "B": c3["B"], "T": c3["T"], "D": c3["D"],
+                                   "fp32 h0/h/h_T", "B": head["B"], "T": head["T"], "D": head["D"],
                        "inputs": "bf16", "parallelism": "single GPU"},
-            "roofline": c3["roofline"],
+            "roofline": head["roofline"],
         })
-        if "cpu_baseline" in c3:
-            out["cpu_baseline"] = c3["cpu_baseline"]
-        extra["scan_launch_ms_mean"] = c3["launch_ms_mean"]
-        extra["scan_launch_ms_min"] = c3["launch_ms_min"]
+        if "cpu_baseline" in head:
+            out["cpu_baseline"] = head["cpu_baseline"]
+        extra["scan_launch_ms_mean"] = head["launch_ms_mean"]
+        extra["scan_launch_ms_min"] = head["launch_ms_min"]
         if "copy_ceiling" in extra:
             out["roofline"]["frac_of_copy_ceiling"] = round(
                 out["roofline"]["achieved"] / extra["copy_ceiling"]["GBps"], 4)

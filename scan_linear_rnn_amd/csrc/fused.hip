@@ -45,7 +45,8 @@ struct FusedParams {
 // Register budget: 4 waves per SIMD (two workgroups per CU), as the plain
 // 256-row GEMM runs.  The scan epilogue then spills a few dozen registers,
 // once per tile; measured 17.3 ms against 19.1 ms at the compiler's own
-// choice (2 waves per SIMD) on the config-4 prefill projection.
+// choice (2 waves per SIMD) on a 131072 x 4096 x 2048 projection (B=256,
+// T=512, D=2048).
 template <bool kDecay, bool kFull>
 __global__ __launch_bounds__(2 * kTileT) __attribute__((amdgpu_waves_per_eu(4)))
 void fused_proj_scan_kernel(const FusedParams F) {

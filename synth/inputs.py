@@ -41,7 +41,8 @@ TENSOR_IDS = {
     "delta_t": 10,
 }
 
-# The five workloads (config index = position + 1).  "N(0, 1/D)" names a
+# The five workloads, keyed by a small integer that is also part of every
+# seed.  "N(0, 1/D)" names a
 # variance, so the standard deviation is D ** -0.5.
 CONFIGS = {
     1: dict(name="tiny_layer_fp32", kind="layer", B=2, T=64, D=16, dtype="f32",

@@ -80,7 +80,7 @@ def test_mingru_backward_f32(B, T, D, with_h0, with_last):
     assert max(errs) < TOL, errs
 
 
-def test_mingru_backward_bf16_reduced_c3():
+def test_mingru_backward_bf16_long_memory_reduced():
     B, T, D = 2, 4096, 1024
     say("mingru bwd bf16")
     cfg = synth.CONFIGS[3]
@@ -161,10 +161,10 @@ def test_minmax_backward_hold_and_reset():
     assert torch.count_nonzero(ds) == B * D
 
 
-def test_full_c3_size_backward_sampled():
+def test_full_size_b8_t65536_d1024_backward_sampled():
     cfg = synth.CONFIGS[3]
     B, T, D = cfg["B"], cfg["T"], cfg["D"]
-    say("full C3 backward")
+    say("full size B=8 T=65536 D=1024 backward")
     kb = synth.device_normal(3, "k", (B, T, D), cfg["k_mean"], cfg["k_std"], torch.bfloat16)
     pb = synth.device_normal(3, "p", (B, T, D), cfg["p_mean"], cfg["p_std"], torch.bfloat16)
     h0 = synth.device_normal(3, "h0", (B, D))
@@ -184,5 +184,5 @@ def test_full_c3_size_backward_sampled():
     errs = _mingru_errors(pick(kb), pick(pb), h0[bs, ds_].double().cpu().numpy()[None],
                           pick(dh), None, dk[bs, :, ds_][None].transpose(1, 2),
                           dp[bs, :, ds_][None].transpose(1, 2), dh0[bs, ds_][None])
-    say("full C3 backward errors", errs)
+    say("full size backward errors", errs)
     assert max(errs) < 1e-4, errs

@@ -58,10 +58,10 @@ def test_decayed_scan_f32(B, T, D, with_h0, log1p, huge):
     assert int(sat.item()) == int(decay.saturated(lam, dt, log1p))
 
 
-def test_decayed_scan_bf16_reduced_c3():
+def test_decayed_scan_bf16_long_memory_reduced():
     cfg = synth.CONFIGS[3]
     B, T, D = 2, 4096, 1024
-    say("decay bf16 reduced C3")
+    say("decay bf16 long-memory B=2 T=4096 D=1024")
     kb = synth.bf16_round(synth.normal_bt(3, "k", B, T, D, cfg["k_mean"], cfg["k_std"])).cuda()
     pb = synth.bf16_round(synth.normal_bt(3, "p", B, T, D, cfg["p_mean"], cfg["p_std"])).cuda()
     h0 = synth.normal_vec(3, "h0", B, D)
@@ -186,10 +186,10 @@ def test_decayed_step_loop_matches_oracle():
     assert metrics.y_rel_err(host64(y), y_ref, hs_ref, W_out) < 1e-4
 
 
-def test_full_c3_size_decayed_sampled():
+def test_full_size_b8_t65536_d1024_decayed_sampled():
     cfg = synth.CONFIGS[3]
     B, T, D = cfg["B"], cfg["T"], cfg["D"]
-    say("decay full C3")
+    say("decay full size B=8 T=65536 D=1024")
     kb = synth.device_normal(3, "k", (B, T, D), cfg["k_mean"], cfg["k_std"], torch.bfloat16)
     pb = synth.device_normal(3, "p", (B, T, D), cfg["p_mean"], cfg["p_std"], torch.bfloat16)
     h0 = synth.device_normal(3, "h0", (B, D))

@@ -41,8 +41,8 @@ def _check_layer(x, W_in, W_out, h0=None, tol=TOL_F32):
 
 
 @pytest.mark.parametrize("cfg_id", [1, 2])
-def test_layer_configs_match_oracle(cfg_id):
-    say(f"layer config {cfg_id}")
+def test_layer_workloads_match_oracle(cfg_id):
+    say(f"layer workload {synth.CONFIGS[cfg_id]['name']}")
     x, W_in, W_out = _layer_inputs(cfg_id)
     y = _check_layer(x, W_in, W_out)
     assert tuple(y.shape) == x.shape  # output has the input's shape
@@ -65,10 +65,10 @@ def test_layer_ragged_shapes(B, T, D_in, D_h, D_out, with_out, with_h0):
 
 
 def test_step_loop_matches_oracle_and_parallel_mode():
-    """Config 2's sequential mode: 1024 token steps from a zero state, each
+    """Sequential mode of the B=2, T=1024, D=512 layer: 1024 token steps from a zero state, each
     checked against the oracle's step, and the final state against the
     parallel forward (the pages' parallel-vs-sequential comparison)."""
-    say("step loop config 2")
+    say("step loop B=2 T=1024 D=512")
     x, W_in, W_out = _layer_inputs(2)
     B, T, D = x.shape
     xd, Wi, Wo = dev(x), dev(W_in), dev(W_out)
@@ -124,15 +124,15 @@ def test_layer_object_api():
     assert tuple(h_t.shape) == (4, 64) and tuple(y_t.shape) == (4, 64)
 
 
-def test_decode_config_4():
-    """Config 4: B=256 streams, D=2048; a parallel prefill of 512 steps, then
+def test_decode_b256_d2048():
+    """Decode workload: B=256 streams, D=2048; a parallel prefill of 512 steps, then
     4096 single-token steps carrying h.  The final state must match the
     parallel forward over the concatenated 4608-step sequence; two seeded
     rows are also checked against the fp64 oracle after steps 1, 2, 8 and at
     the end (the prefill's carry is still visible in the first steps)."""
     cfg = synth.CONFIGS[4]
     B, D, Tp, S = cfg["B"], cfg["D"], cfg["T_prefill"], cfg["steps"]
-    say("decode config 4")
+    say("decode B=256 D=2048")
     W_in = synth.device_normal(4, "W_in", (D, 2 * D), 0.0, cfg["w_std"])
     W_out = synth.device_normal(4, "W_out", (D, D), 0.0, cfg["w_std"])
     x = synth.device_normal(4, "x", (B, Tp + S, D))

@@ -35,10 +35,10 @@ def test_minmax_bitwise(B, T, D):
     assert metrics.bits_equal(last.cpu().numpy(), ref_last)
 
 
-def test_minmax_full_c5_bitwise():
+def test_minmax_full_size_b8_t32768_d192_bitwise():
     cfg = synth.CONFIGS[5]
     B, T, D = cfg["B"], cfg["T"], cfg["D"]
-    say("minmax full C5")
+    say("minmax full size B=8 T=32768 D=192")
     r = synth.uniform_bt(5, "r", B, T, D, -1.0, 1.0)
     s = synth.uniform_bt(5, "s", B, T, D, -1.0, 1.0) - np.float32(0.5)
     s[s == 0] = 0.0

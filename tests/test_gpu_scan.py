@@ -41,9 +41,9 @@ def test_scan_f32_matches_oracle(B, T, D, with_h0):
     assert np.array_equal(host64(last), host64(y)[:, -1, :])
 
 
-def test_scan_bf16_reduced_c3_statistics():
+def test_scan_bf16_long_memory_statistics():
     B, T, D = 2, 4096, 1024
-    say(f"scan bf16 reduced C3 B={B} T={T} D={D}")
+    say(f"scan bf16 long-memory B={B} T={T} D={D}")
     cfg = synth.CONFIGS[3]
     k32 = synth.normal_bt(3, "k", B, T, D, cfg["k_mean"], cfg["k_std"])
     p32 = synth.normal_bt(3, "p", B, T, D, cfg["p_mean"], cfg["p_std"])
@@ -127,14 +127,14 @@ def test_empty_sequence_returns_carried_state():
     assert torch.count_nonzero(last) == 0
 
 
-def test_full_c3_size_sampled_channels():
+def test_full_size_b8_t65536_d1024_sampled_channels():
     """The bench workload at full size (B=8, T=65536, D=1024, bf16 inputs),
     launched exactly as the benchmark launches it; 24 sampled channels are
     checked over all 65536 steps against the oracle, and every output must be
     finite."""
     cfg = synth.CONFIGS[3]
     B, T, D = cfg["B"], cfg["T"], cfg["D"]
-    say("full C3 sampled")
+    say("full size B=8 T=65536 D=1024 sampled")
     kb = synth.device_normal(3, "k", (B, T, D), cfg["k_mean"], cfg["k_std"], torch.bfloat16)
     pb = synth.device_normal(3, "p", (B, T, D), cfg["p_mean"], cfg["p_std"], torch.bfloat16)
     h0 = synth.device_normal(3, "h0", (B, D))
@@ -151,7 +151,7 @@ def test_full_c3_size_sampled_channels():
     hh0 = h0[bs, ds].double().cpu().numpy()[None]
     got = y[bs, :, ds].double().cpu().numpy()[None].transpose(0, 2, 1)
     err = scan_err(got, k, p, hh0)
-    say("full C3 sampled err", err)
+    say("full size sampled err", err)
     assert err < TOL_BF16 and err < 1e-5
     ref_last = mingru.scan(k, p, hh0)[0, -1]
     assert np.max(np.abs(last[bs, ds].double().cpu().numpy() - ref_last)) < 1e-5
