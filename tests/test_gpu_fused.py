@@ -36,6 +36,7 @@ def _case(B, T, D_in, D_h, D_out, seed):
     (2, 4100, 16, 2048, 2048, False, True),    # a 4-step last tile
     (4, 2048, 96, 2048, 512, True, False),
     (1, 16384, 32, 512, 512, False, True),     # one batch row, 64 tiles along T
+    (64, 5, 24, 512, 256, True, True),         # one partial tile per chain: 5 of 256 steps
 ])
 def test_fused_forward_matches_oracle(B, T, D_in, D_h, D_out, with_out, with_h0):
     say(f"fused B={B} T={T} D_in={D_in} D_h={D_h} D_out={D_out} out={with_out} h0={with_h0}")
@@ -94,3 +95,24 @@ def test_fused_decayed_forward_matches_oracle():
         say("log1p", log1p, "error", err)
         assert err < TOL_F32
         assert int(sat.item()) == int(decay.saturated(lam, dt, log1p))
+
+
+def test_fused_decayed_with_output_projection():
+    """Decay, W_in and W_out together (the fused projection + scan, then the
+    output GEMM) against the oracle layer."""
+    B, T, D_in, D_h, D_out = 8, 1024, 48, 1024, 320
+    say("fused decayed with W_out")
+    assert _fused_taken(B, T, D_in, D_h, D_out, True)
+    x, W_in, W_out, h0 = _case(B, T, D_in, D_h, D_out, seed=13)
+    rng = np.random.default_rng(1302)
+    lam = (10.0 ** rng.uniform(-2, 0, D_h)).astype(np.float32)
+    dt = rng.exponential(0.5, (B, T)).astype(np.float32)
+    y, last = sr.mingru_forward_decayed(dev(x), dev(W_in), decay_rate=dev(lam), delta_t=dev(dt),
+                                        h0=dev(h0), W_out=dev(W_out), return_last=True)
+    y_ref, h_ref, last_ref = decay.layer(x, W_in, lam, dt, W_out, h0)
+    err = metrics.y_rel_err(host64(y), y_ref, h_ref, W_out)
+    k, p = mingru.layer_kp(x, W_in)
+    carry, inp = decay.scan_terms(k, p, lam, dt, h0)
+    last_err = metrics.h_rel_err(host64(last), last_ref, carry[:, -1], inp[:, -1])
+    say("errors", err, last_err)
+    assert err < TOL_F32 and last_err < TOL_F32
