@@ -135,8 +135,22 @@ __global__ __launch_bounds__(64 * kSmallSlices) void small_m_kernel(const GemmPa
 #pragma unroll
   for (int m = 0; m < MR; ++m) acc[m] = 0.0f;
   if (col_ok) {
-    for (int64_t k = k0; k < k1; ++k) {
-      const float b = P.Bm[k * P.ldb + col];
+    // Eight B loads in flight per round (the loop is latency-bound: a few
+    // dozen iterations per thread).
+    const float* bp = P.Bm + k0 * P.ldb + col;
+    int64_t k = k0;
+    for (; k + 8 <= k1; k += 8, bp += 8 * P.ldb) {
+      float b[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) b[u] = bp[u * P.ldb];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int m = 0; m < MR; ++m)
+          if (m < P.M) acc[m] = fmaf(P.A[m * P.lda + k + u], b[u], acc[m]);
+    }
+    for (; k < k1; ++k, bp += P.ldb) {
+      const float b = *bp;
 #pragma unroll
       for (int m = 0; m < MR; ++m)
         if (m < P.M) acc[m] = fmaf(P.A[m * P.lda + k], b, acc[m]);
