@@ -165,6 +165,19 @@ def _workspace(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
+def _use_workspace(workspace, nbytes: int, device) -> torch.Tensor:
+    """The caller's workspace (checked), or a fresh one when none is given."""
+    if workspace is None:
+        return _workspace(nbytes, device)
+    if not isinstance(workspace, torch.Tensor) or workspace.dtype != torch.uint8:
+        raise TypeError("workspace must be a torch.uint8 tensor")
+    if workspace.device != torch.device(device) or not workspace.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {device}")
+    if workspace.numel() < nbytes:
+        raise ValueError(f"workspace has {workspace.numel()} bytes, {nbytes} needed")
+    return workspace
+
+
 def mingru_forward(x=None, W_in=None, *, k=None, p=None, h0=None, W_out=None,
                    return_last=False, workspace=None, out=None, out_last=None):
     """Parallel mode over a whole sequence.
@@ -266,7 +279,7 @@ def _forward(x, W_in, k, p, h0, W_out, return_last, workspace, out, out_last, de
             h_last = torch.empty((B, D_h), dtype=torch.float32, device=device)
     nbytes = _lib.mingru_forward_workspace_size(B, T, D_in, D_h, D_out, int(W_in is not None),
                                                 int(W_out is not None))
-    ws = workspace if workspace is not None and workspace.numel() >= nbytes else _workspace(nbytes, device)
+    ws = _use_workspace(workspace, nbytes, device)
     if decay is None:
         st = _lib.mingru_forward(B, T, D_in, D_h, D_out, _ptr(x if W_in is not None else None),
                                  _ptr(W_in), _ptr(kk), _ptr(pp), ld_kp, kp_dtype, _ptr(h0),
@@ -333,7 +346,7 @@ def _step(x_t, W_in, W_out, h_prev, h_next, workspace, decay):
     nbytes = _lib.mingru_step_workspace_size(B, D_in, D_h, D_out)
     ws = None
     if nbytes:
-        ws = workspace if workspace is not None and workspace.numel() >= nbytes else _workspace(nbytes, device)
+        ws = _use_workspace(workspace, nbytes, device)
     if decay is None:
         st = _lib.mingru_step(B, D_in, D_h, D_out, _ptr(x_t), _ptr(W_in), _ptr(W_out),
                               _ptr(h_prev), _ptr(h_next), _ptr(y_t), _ptr(ws),
@@ -373,7 +386,7 @@ def minmax_scan(r, s, x0, return_last=False, workspace=None, out=None, out_last=
         else:
             last = torch.empty((B, D), dtype=torch.float32, device=r.device)
     nbytes = _lib.minmax_scan_workspace_size(B, T, D)
-    ws = workspace if workspace is not None and workspace.numel() >= nbytes else _workspace(nbytes, r.device)
+    ws = _use_workspace(workspace, nbytes, r.device)
     st = _lib.minmax_scan(B, T, D, _ptr(r), _ptr(s), _ptr(x0), _ptr(out), _ptr(last), _ptr(ws),
                           ws.numel(), _stream(r.device))
     _check("minmax_scan", st)
@@ -428,7 +441,7 @@ def mingru_scan_backward(k, p, h, dh, h0=None, dh_last=None, workspace=None):
     dp = torch.empty_like(dk)
     dh0 = torch.empty((B, D), dtype=torch.float32, device=k.device) if h0 is not None else None
     nbytes = _lib.mingru_scan_backward_workspace_size(B, T, D)
-    ws = workspace if workspace is not None and workspace.numel() >= nbytes else _workspace(nbytes, k.device)
+    ws = _use_workspace(workspace, nbytes, k.device)
     st = _lib.mingru_scan_backward(B, T, D, _ptr(k), _ptr(p), k.stride(1),
                                    SR_BF16 if k.dtype == torch.bfloat16 else SR_F32, _ptr(h0),
                                    _ptr(h), _ptr(dh), _ptr(dh_last), _ptr(dk), _ptr(dp), _ptr(dh0),
@@ -451,7 +464,7 @@ def minmax_scan_backward(r, s, x0, x_out, dx, dx_last=None, workspace=None):
     ds = torch.empty_like(r)
     dx0 = torch.empty((B, D), dtype=torch.float32, device=r.device)
     nbytes = _lib.minmax_scan_backward_workspace_size(B, T, D)
-    ws = workspace if workspace is not None and workspace.numel() >= nbytes else _workspace(nbytes, r.device)
+    ws = _use_workspace(workspace, nbytes, r.device)
     st = _lib.minmax_scan_backward(B, T, D, _ptr(r), _ptr(s), _ptr(x0), _ptr(x_out), _ptr(dx),
                                    _ptr(dx_last), _ptr(dr), _ptr(ds), _ptr(dx0), _ptr(ws),
                                    ws.numel(), _stream(r.device))

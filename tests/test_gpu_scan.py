@@ -155,3 +155,18 @@ def test_full_size_b8_t65536_d1024_sampled_channels():
     assert err < TOL_BF16 and err < 1e-5
     ref_last = mingru.scan(k, p, hh0)[0, -1]
     assert np.max(np.abs(last[bs, ds].double().cpu().numpy() - ref_last)) < 1e-5
+
+
+def test_caller_workspace_is_checked():
+    """A workspace passed by the caller is used as given or rejected, never
+    silently replaced."""
+    k = torch.zeros((2, 300, 64), device="cuda")
+    n = sr.raw_library().mingru_forward_workspace_size(2, 300, 0, 64, 64, 0, 0)
+    good = torch.empty(n, dtype=torch.uint8, device="cuda")
+    sr.mingru_forward(k=k, p=k, workspace=good)
+    with pytest.raises(ValueError):
+        sr.mingru_forward(k=k, p=k, workspace=good[: n - 1])
+    with pytest.raises(TypeError):
+        sr.mingru_forward(k=k, p=k, workspace=torch.empty(n, device="cuda"))
+    with pytest.raises(ValueError):
+        sr.minmax_scan(k, k, torch.zeros((2, 64), device="cuda"), workspace=good[:16])
