@@ -86,6 +86,7 @@ def scan(k, p, decay_rate, delta_t, h0=None, log1p_delta=False):
     k = _f64(k)
     p = _f64(p)
     z = scalar.sigmoid(k)
+    a = scalar.sigmoid(-k)  # = 1 - z, without cancelling
     htilde = scalar.g(p)
     gam = gamma(decay_rate, delta_t, log1p_delta)
     B, T, D = k.shape
@@ -93,7 +94,7 @@ def scan(k, p, decay_rate, delta_t, h0=None, log1p_delta=False):
     out = np.empty((B, T, D))
     for t in range(T):
         h = gam[:, t, :] * h                               # the token boundary
-        h = (1.0 - z[:, t, :]) * h + z[:, t, :] * htilde[:, t, :]  # the token's write
+        h = a[:, t, :] * h + z[:, t, :] * htilde[:, t, :]  # the token's write
         out[:, t, :] = h
     return out
 
@@ -102,11 +103,10 @@ def scan_terms(k, p, decay_rate, delta_t, h0=None, log1p_delta=False):
     """(|prod (1 - z) gamma| |h_0|, response to a zero h_0): the sizes of the two
     non-negative terms h is the sum of, for the conditioned error measure."""
     k = _f64(k)
-    z = scalar.sigmoid(k)
     input_term = scan(k, p, decay_rate, delta_t, None, log1p_delta)
     if h0 is None:
         return np.zeros_like(input_term), input_term
-    coef = np.cumprod((1.0 - z) * gamma(decay_rate, delta_t, log1p_delta), axis=1)
+    coef = np.cumprod(scalar.sigmoid(-k) * gamma(decay_rate, delta_t, log1p_delta), axis=1)
     return coef * np.abs(_f64(h0))[:, None, :], input_term
 
 
@@ -124,6 +124,6 @@ def step(x_t, W_in, decay_rate, delta_t, W_out=None, h_prev=None, log1p_delta=Fa
     z = scalar.sigmoid(k)
     gam = gamma(decay_rate, _f64(delta_t)[:, None], log1p_delta)[:, 0, :]
     h = np.zeros_like(z) if h_prev is None else _f64(h_prev)
-    h_t = (1.0 - z) * (gam * h) + z * scalar.g(p)
+    h_t = scalar.sigmoid(-_f64(k)) * (gam * h) + z * scalar.g(p)
     y_t = h_t if W_out is None else mingru.project(h_t, W_out)
     return y_t, h_t

@@ -45,7 +45,7 @@ def mingru_scan_backward(k, p, h0, dh, dh_last=None):
     dh = _f64(dh)
     B, T, D = k.shape
     z = scalar.sigmoid(k)
-    a = 1.0 - z
+    a = scalar.sigmoid(-k)  # = 1 - z, without cancelling
     gp = scalar.g(p)
     # forward states h_{t-1} entering each step
     h = np.zeros((B, D)) if h0 is None else _f64(h0).copy()

@@ -68,12 +68,13 @@ def scan(k, p, h0=None):
     k = _f64(k)
     p = _f64(p)
     z = scalar.sigmoid(k)
+    a = scalar.sigmoid(-k)  # = 1 - z (log(1 - z) = -softplus(k)), without cancelling
     htilde = scalar.g(p)
     B, T, D = k.shape
     h = np.zeros((B, D)) if h0 is None else _f64(h0).copy()
     out = np.empty((B, T, D))
     for t in range(T):
-        h = (1.0 - z[:, t, :]) * h + z[:, t, :] * htilde[:, t, :]
+        h = a[:, t, :] * h + z[:, t, :] * htilde[:, t, :]
         out[:, t, :] = h
     return out
 
@@ -86,12 +87,11 @@ def scan_terms(k, p, h0=None):
     quantities h_t is computed from, and conditions the relative error.
     """
     k = _f64(k)
-    z = scalar.sigmoid(k)
     input_term = scan(k, p, None)
     if h0 is None:
         carry = np.zeros_like(input_term)
     else:
-        decay = np.cumprod(1.0 - z, axis=1)
+        decay = np.cumprod(scalar.sigmoid(-k), axis=1)  # prod (1 - z)
         carry = decay * np.abs(_f64(h0))[:, None, :]
     return carry, input_term
 
@@ -123,6 +123,6 @@ def step(x_t, W_in, W_out=None, h_prev=None):
     z = scalar.sigmoid(k)
     htilde = scalar.g(p)
     h = np.zeros_like(z) if h_prev is None else _f64(h_prev)
-    h_t = (1.0 - z) * h + z * htilde
+    h_t = scalar.sigmoid(-k) * h + z * htilde  # sigma(-k) = 1 - z
     y_t = h_t if W_out is None else project(h_t, W_out)
     return y_t, h_t

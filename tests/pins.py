@@ -135,10 +135,11 @@ def scan_mp_err(scan, seed=0, T=12, D=3, with_h0=True, k_mean=0.0) -> float:
 
 
 def closed_z1_err(scan, g) -> float:
-    """k = +40: sigma(k) rounds to exactly 1 in float64, so h_t = g(p_t)."""
+    """k = +800: sigma(k) is exactly 1 and sigma(-k) exactly 0 in float64
+    (e^-800 underflows), so h_t = g(p_t)."""
     rng = np.random.default_rng(21)
     p = rng.normal(0.0, 3.0, (2, 50, 4))
-    k = np.full_like(p, 40.0)
+    k = np.full_like(p, 800.0)
     h0 = rng.normal(0.0, 1.0, (2, 4))
     h = scan(k, p, h0)
     return float(np.max(np.abs(h - g(p))))

@@ -17,7 +17,7 @@ TOL = 1e-4
 
 def _abs_G(k, dh, dh_last):
     """|G|-bound: the reverse recurrence run on |dh| (every term non-negative)."""
-    a = 1.0 - scalar.sigmoid(k)
+    a = scalar.sigmoid(-np.asarray(k, np.float64))  # 1 - sigma(k)
     B, T, D = k.shape
     G = np.zeros((B, D)) if dh_last is None else np.abs(dh_last)
     out = np.empty((B, T, D))
@@ -36,7 +36,7 @@ def _mingru_errors(k, p, h0, dh, dl, dk, dp, dh0):
     rdk, rdp, rdh0 = grad.mingru_scan_backward(k, p, h0, dh, dl)
     Gabs = _abs_G(k, dh, dl)
     z = scalar.sigmoid(k)
-    a = 1.0 - z
+    a = scalar.sigmoid(-k)  # 1 - z
     g = scalar.g(p)
     B, T, D = k.shape
     h = np.zeros((B, D)) if h0 is None else np.asarray(h0, np.float64).copy()

@@ -83,8 +83,9 @@ def test_mingru_backward_closed_forms():
     dk, dp, dh0 = grad.mingru_scan_backward(np.full((B, T, D), -40.0), p, h0, dh, dl)
     assert np.allclose(dh0, dh.sum(axis=1) + dl, rtol=1e-13, atol=1e-13)
     assert np.max(np.abs(dk)) < 1e-15 and np.max(np.abs(dp)) < 1e-15
-    # z = 1 exactly (k = +40): h_t = g(p_t), nothing flows to h_0 or across steps.
-    dk, dp, dh0 = grad.mingru_scan_backward(np.full((B, T, D), 40.0), p, h0, dh, dl)
+    # z = 1 exactly (k = +800: 1 - z = e^-800 / (1 + e^-800) is 0 in fp64; at
+    # k = +40 it is 4e-18, not 0): h_t = g(p_t), nothing flows to h_0 or across steps.
+    dk, dp, dh0 = grad.mingru_scan_backward(np.full((B, T, D), 800.0), p, h0, dh, dl)
     G = dh.copy()
     G[:, -1] += dl
     assert np.array_equal(dh0, np.zeros_like(dh0)) and np.array_equal(dk, np.zeros_like(dk))
