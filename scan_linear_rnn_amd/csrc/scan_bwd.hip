@@ -207,7 +207,9 @@ void scan_backward_kernel(const BwdParams Q) {
         float z, a, g, gs;
         sig_pair(kt[c], z, a);
         g_and_slope(pt[c], g, gs);
-        o0v[c] = G[c] * z * a * (g - h_prev);
+        // z a first, then the difference, then G: z a can sit at the bottom
+        // of the normal range (|k| near 87), and G z a would go subnormal.
+        o0v[c] = ((z * a) * (g - h_prev)) * G[c];
         o1v[c] = G[c] * z * gs;
         pass_or_a[c] = a;
       }

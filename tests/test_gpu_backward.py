@@ -186,3 +186,25 @@ def test_full_size_b8_t65536_d1024_backward_sampled():
                           dp[bs, :, ds_][None].transpose(1, 2), dh0[bs, ds_][None])
     say("full size backward errors", errs)
     assert max(errs) < 1e-4, errs
+
+
+def test_mingru_backward_extreme_values():
+    """Gate logits up to |k| = 87 (both sigmoids stay normal fp32 numbers),
+    candidates up to 1e30, against the fp64 oracle with the conditioned
+    errors (their floors keep outputs far below the fp32 range out of the
+    relative measure)."""
+    rng = np.random.default_rng(1140)
+    B, T, D = 2, 2000, 130
+    k = rng.choice([-87.0, -80.0, -30.0, -3.0, 0.0, 3.0, 30.0, 80.0, 87.0], (B, T, D)).astype(np.float32)
+    p = rng.choice([-1e4, -100.0, -20.0, -1.0, 0.0, 1.0, 20.0, 1e6, 1e30], (B, T, D)).astype(np.float32)
+    h0 = rng.choice([-1e6, -1.0, 0.0, 1.0, 1e6], (B, D)).astype(np.float32)
+    dh = rng.standard_normal((B, T, D)).astype(np.float32)
+    dl = rng.standard_normal((B, D)).astype(np.float32)
+    say("mingru bwd extremes")
+    kd, pd, h0d = dev(k), dev(p), dev(h0)
+    h = sr.mingru_forward(k=kd, p=pd, h0=h0d)
+    dk, dp, dh0 = sr.mingru_scan_backward(kd, pd, h, dev(dh), h0=h0d, dh_last=dev(dl))
+    assert bool(torch.isfinite(dk).all() and torch.isfinite(dp).all() and torch.isfinite(dh0).all())
+    errs = _mingru_errors(k, p, h0, dh, dl, dk, dp, dh0)
+    say("errors", errs)
+    assert max(errs) < TOL, errs
