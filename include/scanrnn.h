@@ -68,8 +68,10 @@ typedef enum {
 typedef enum { SR_F32 = 0, SR_BF16 = 1 } sr_dtype;
 
 /* Bytes of workspace mingru_forward needs.  has_w_in / has_w_out say whether
- * the call will pass W_in / W_out (the projections need staging buffers:
- * B*T*2*D_h floats for [k|p], B*T*D_h floats for h). */
+ * the call will pass W_in / W_out.  W_out needs B*T*D_h floats to stage h.
+ * With W_in, large problems (at least 512 tiles of 256 steps x 64 channels)
+ * compute the projection inside the scan and need no more; smaller ones
+ * stage [k|p] (B*T*2*D_h floats) and split-K partial sums. */
 size_t mingru_forward_workspace_size(int64_t B, int64_t T, int64_t D_in, int64_t D_h,
                                      int64_t D_out, int has_w_in, int has_w_out);
 
