@@ -167,3 +167,41 @@ def test_step_decayed_rejects_bad_arguments():
     assert f(*args, FAKE, None, 0, None, *tail) == sr.SR_ERR_INVALID_ARGUMENT
     assert f(*args, FAKE, FAKE, 5, None, *tail) == sr.SR_ERR_INVALID_ARGUMENT
     assert f(*args, FAKE, FAKE, 1, None, *tail) == sr.SR_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_header_is_plain_c_and_links(tmp_path):
+    """The header compiles as C11 and a C program linked against the library
+    gets the documented validation errors (no GPU needed: nothing launches)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "abi_check.c"
+    src.write_text(r'''
+#include <stdio.h>
+#include "scanrnn.h"
+int main(void) {
+  float* fake = (float*)0x10000;
+  if (mingru_forward(-1, 4, 0, 4, 4, 0, 0, fake, fake, 4, SR_F32, 0, 0, fake, 0, fake, 1u << 20, 0)
+      != SR_ERR_INVALID_ARGUMENT) return 1;
+  if (scanrnn_last_error()[0] == '\0') return 2;
+  if (minmax_scan(2, 8, 4, fake, fake, 0, fake, 0, fake, 1u << 20, 0) != SR_ERR_INVALID_ARGUMENT)
+    return 3;
+  if (mingru_forward_workspace_size(8, 65536, 0, 1024, 1024, 0, 0) == 0) return 4;
+  printf("%s\n", scanrnn_version());
+  return 0;
+}
+''')
+    lib = sr.library_path()
+    exe = tmp_path / "abi_check"
+    subprocess.run([cc, "-std=c11", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
+                    str(src), lib, f"-Wl,-rpath,{os.path.dirname(lib)}", "-o", str(exe)],
+                   check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert out.returncode == 0, (out.returncode, out.stderr)
+    assert out.stdout.strip() == lib_version()
+
+
+def lib_version():
+    return lib.scanrnn_version().decode()
