@@ -298,14 +298,40 @@ def leg_layer(torch, sr, synth, cfg_id, steps):
     res = dict(B=B, T=T, D=D, forward_ms=wall / steps * 1e3, forward_launch_ms=mean_ms,
                elements_per_s=B * T * D / (wall / steps))
     xs = [x[:, t].contiguous() for t in range(T)]
+
+    def loop():
+        h = None
+        for t in range(T):
+            _, h = sr.mingru_step(xs[t], W_in, W_out, h_prev=h)
+        return h
+
+    loop()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    h = None
-    for t in range(T):
-        _, h = sr.mingru_step(xs[t], W_in, W_out, h_prev=h)
+    loop()
     torch.cuda.synchronize()
-    res["step_loop_ms"] = (time.perf_counter() - t0) * 1e3
-    res["steps_per_s"] = T / (time.perf_counter() - t0)
+    dt = time.perf_counter() - t0
+    res["step_loop_ms"] = dt * 1e3
+    res["steps_per_s"] = T / dt
+    # The same token loop captured once in a HIP graph and replayed (the
+    # launch-bound regime: a few tiny kernels per token).
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        loop()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        loop()
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g.replay()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    res["graph_step_loop_ms"] = dt * 1e3
+    res["graph_steps_per_s"] = T / dt
+    del g
     return res
 
 

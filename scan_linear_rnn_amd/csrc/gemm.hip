@@ -108,35 +108,38 @@ __global__ __launch_bounds__(2 * TBM) void gemm_f32_kernel(const GemmParams P) {
 
 // Products with at most kSmallM rows (a step over a few streams): a
 // 128-row MFMA tile would spend its whole K loop on them, so they run on
-// fp32 FMAs instead.  A workgroup of 1024 threads owns 64 columns (step
-// mode: 32 channels, k then p) and all rows; thread (c, s) accumulates
-// column c over the s-th of 16 K slices, and the slices are summed in LDS
-// in slice order (deterministic), then stored or used by the step update.
+// fp32 FMAs instead.  A workgroup of 1024 threads owns CB columns (step
+// mode: CB/2 channels, k then p) and all rows; thread (c, s) accumulates
+// column c over the s-th of 1024/CB K slices, and the slices are summed in
+// LDS in slice order (deterministic), then stored or used by the step
+// update.  Narrower column blocks give more workgroups and shorter K loops
+// (the loop is latency-bound: a few dozen loads per thread).
 constexpr int kSmallM = 16;
-constexpr int kSmallSlices = 16;
+constexpr int kSmallThreads = 1024;
 
-template <int MODE, int MR>
-__global__ __launch_bounds__(64 * kSmallSlices) void small_m_kernel(const GemmParams P) {
-  __shared__ float red[kSmallSlices][MR][64];
-  const int c = threadIdx.x & 63, sl = threadIdx.x >> 6;
+template <int MODE, int MR, int CB>
+__global__ __launch_bounds__(kSmallThreads) void small_m_kernel(const GemmParams P) {
+  constexpr int SL = kSmallThreads / CB;  // K slices
+  constexpr int HC = CB / 2;              // step mode: channels per block
+  __shared__ float red[SL][MR][CB];
+  const int c = threadIdx.x % CB, sl = threadIdx.x / CB;
   int64_t col;
   bool col_ok;
   if (MODE == kPlain) {
-    col = int64_t(blockIdx.x) * 64 + c;
+    col = int64_t(blockIdx.x) * CB + c;
     col_ok = col < P.N;
   } else {
-    const int64_t ch = int64_t(blockIdx.x) * 32 + (c & 31);
-    col = (c < 32 ? 0 : P.D_h) + ch;
+    const int64_t ch = int64_t(blockIdx.x) * HC + (c % HC);
+    col = (c < HC ? 0 : P.D_h) + ch;
     col_ok = ch < P.D_h;
   }
-  const int64_t ks = (P.K + kSmallSlices - 1) / kSmallSlices;
+  const int64_t ks = (P.K + SL - 1) / SL;
   const int64_t k0 = sl * ks, k1 = (k0 + ks < P.K) ? k0 + ks : P.K;
   float acc[MR];
 #pragma unroll
   for (int m = 0; m < MR; ++m) acc[m] = 0.0f;
   if (col_ok) {
-    // Eight B loads in flight per round (the loop is latency-bound: a few
-    // dozen iterations per thread).
+    // Eight B loads in flight per round.
     const float* bp = P.Bm + k0 * P.ldb + col;
     int64_t k = k0;
     for (; k + 8 <= k1; k += 8, bp += 8 * P.ldb) {
@@ -160,18 +163,24 @@ __global__ __launch_bounds__(64 * kSmallSlices) void small_m_kernel(const GemmPa
   for (int m = 0; m < MR; ++m) red[sl][m][c] = acc[m];
   __syncthreads();
   // Thread (c, m): the slices of (row m, column c), in order.
-  const int m = threadIdx.x >> 6;
-  if (m < MR && m < P.M) {
-    float v = 0.0f;
-#pragma unroll
-    for (int q = 0; q < kSmallSlices; ++q) v += red[q][m][c];
-    if (MODE == kPlain) {
-      if (col_ok) P.C[m * P.ldc + col] = v;
-    } else if (c < 32 && col_ok) {
-      float vp = 0.0f;
-#pragma unroll
-      for (int q = 0; q < kSmallSlices; ++q) vp += red[q][m][c + 32];
-      step_update(P, m, int64_t(blockIdx.x) * 32 + c, v, vp);
+  if (threadIdx.x < CB * MR) {
+    const int rc = threadIdx.x % CB, m = threadIdx.x / CB;
+    if (m < P.M) {
+      float v = 0.0f;
+#pragma unroll 8
+      for (int q = 0; q < SL; ++q) v += red[q][m][rc];
+      if (MODE == kPlain) {
+        const int64_t oc = int64_t(blockIdx.x) * CB + rc;
+        if (oc < P.N) P.C[m * P.ldc + oc] = v;
+      } else if (rc < HC) {
+        const int64_t ch = int64_t(blockIdx.x) * HC + rc;
+        if (ch < P.D_h) {
+          float vp = 0.0f;
+#pragma unroll 8
+          for (int q = 0; q < SL; ++q) vp += red[q][m][rc + HC];
+          step_update(P, m, ch, v, vp);
+        }
+      }
     }
   }
 }
@@ -230,18 +239,31 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, bool step) {
 
 namespace {
 
+template <int MODE, int CB>
+void launch_small_m_cb(const GemmParams& P, int64_t n_cols, hipStream_t stream) {
+  const int64_t blocks = (n_cols + (MODE == kPlain ? CB : CB / 2) - 1) / (MODE == kPlain ? CB : CB / 2);
+  const dim3 grid{uint32_t(blocks)}, block{kSmallThreads};
+  if (P.M <= 2)
+    hipLaunchKernelGGL((small_m_kernel<MODE, 2, CB>), grid, block, 0, stream, P);
+  else if (P.M <= 4)
+    hipLaunchKernelGGL((small_m_kernel<MODE, 4, CB>), grid, block, 0, stream, P);
+  else if (P.M <= 8)
+    hipLaunchKernelGGL((small_m_kernel<MODE, 8, CB>), grid, block, 0, stream, P);
+  else
+    hipLaunchKernelGGL((small_m_kernel<MODE, kSmallM, CB>), grid, block, 0, stream, P);
+}
+
 template <int MODE>
 hipError_t launch_small_m(const GemmParams& P, hipStream_t stream) {
-  const int64_t blocks = MODE == kPlain ? (P.N + 63) / 64 : (P.D_h + 31) / 32;
-  const dim3 grid{uint32_t(blocks)}, block{64 * kSmallSlices};
-  if (P.M <= 2)
-    hipLaunchKernelGGL((small_m_kernel<MODE, 2>), grid, block, 0, stream, P);
-  else if (P.M <= 4)
-    hipLaunchKernelGGL((small_m_kernel<MODE, 4>), grid, block, 0, stream, P);
-  else if (P.M <= 8)
-    hipLaunchKernelGGL((small_m_kernel<MODE, 8>), grid, block, 0, stream, P);
+  // The widest column block that still gives 64 workgroups (16 at least).
+  const int64_t n_cols = MODE == kPlain ? P.N : P.D_h;   // columns, or channels in step mode
+  const int64_t per64 = MODE == kPlain ? 64 : 32, per32 = per64 / 2;
+  if ((n_cols + per64 - 1) / per64 >= 64)
+    launch_small_m_cb<MODE, 64>(P, n_cols, stream);
+  else if ((n_cols + per32 - 1) / per32 >= 64)
+    launch_small_m_cb<MODE, 32>(P, n_cols, stream);
   else
-    hipLaunchKernelGGL((small_m_kernel<MODE, kSmallM>), grid, block, 0, stream, P);
+    launch_small_m_cb<MODE, 16>(P, n_cols, stream);
   return hipGetLastError();
 }
 
