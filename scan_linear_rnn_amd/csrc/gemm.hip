@@ -31,15 +31,11 @@ __device__ __forceinline__ float g_act(float p) {
   return p >= 0.0f ? p + 0.5f : ep * __builtin_amdgcn_rcpf(1.0f + ep);
 }
 
-// h_next = (1 - z) h_prev + z g(p) with z = sigma(k), for one (row, channel).
-// With time decay the carried state is first scaled by
-// exp(-min(rate_d * gap_row, 1e4)) (the token boundary comes before the
-// token's write; exp(-1e4) is zero in float32, so the clamp changes no value
-// and only marks saturation).
-__device__ __forceinline__ void step_update(const GemmParams& P, int64_t row, int64_t d, float k,
-                                            float p) {
-  float a;
-  const float z = sigmoid_pos_neg(k, a);
+// The carried state entering the step for one (row, channel): h_prev (zero
+// when absent), with time decay first scaled by exp(-min(rate_d * gap_row,
+// 1e4)) (the token boundary comes before the token's write; exp(-1e4) is
+// zero in float32, so the clamp changes no value and only marks saturation).
+__device__ __forceinline__ float carried_state(const GemmParams& P, int64_t row, int64_t d) {
   float hp = P.h_prev ? P.h_prev[row * P.D_h + d] : 0.0f;
   if (P.rate != nullptr) {
     constexpr float kClamp = 1.0e4f, kLog2e = 1.4426950408889634f;
@@ -49,7 +45,19 @@ __device__ __forceinline__ void step_update(const GemmParams& P, int64_t row, in
       __hip_atomic_fetch_or(P.saturated, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     hp *= __builtin_amdgcn_exp2f(fminf(e, kClamp) * -kLog2e);
   }
-  P.h_next[row * P.D_h + d] = fmaf(a, hp, z * g_act(p));
+  return hp;
+}
+
+// h_next = (1 - z) h + z g(p) with z = sigma(k), h the carried state.
+__device__ __forceinline__ float step_value(float k, float p, float h) {
+  float a;
+  const float z = sigmoid_pos_neg(k, a);
+  return fmaf(a, h, z * g_act(p));
+}
+
+__device__ __forceinline__ void step_update(const GemmParams& P, int64_t row, int64_t d, float k,
+                                            float p) {
+  P.h_next[row * P.D_h + d] = step_value(k, p, carried_state(P, row, d));
 }
 
 // One TBM x 128 tile per workgroup; blockIdx.x numbers the tiles (N tiles
@@ -185,6 +193,255 @@ __global__ __launch_bounds__(kSmallThreads) void small_m_kernel(const GemmParams
   }
 }
 
+// Products with a few hundred rows (the step over a batch of streams): the
+// 128 x 128 tiles would be too few to fill the part, and splitting K across
+// workgroups costs a round trip of the slices' sums through HBM.  Instead a
+// workgroup owns a narrow tile of TM (64 or 32) rows x 64 columns (step
+// mode: the k and p columns of 32 channels, so that a lane holds k and p of
+// the same (row, d)) and splits K over its KG waves: wave g computes the
+// whole tile (TM / 32 x 2 MFMA tiles of 32 x 32) over the g-th share of K,
+// staged through its own LDS buffers.  The waves' sums meet in LDS and are
+// added in wave order (deterministic), by all threads, which then store or
+// apply the step update.
+constexpr int kNarrowCols = 64;
+constexpr int kNarrowMaxM = 512;
+constexpr int kNarrowKG = 8;  // waves (K groups) per workgroup
+constexpr int kNarrowSK = 16; // K per pipeline stage
+
+template <int TM>
+struct Narrow {
+  static constexpr int kRI = TM / 32;                       // row blocks per wave
+  static constexpr int kThreads = 64 * kNarrowKG;
+  static constexpr int kAPer = TM * kNarrowSK / 64;         // A floats per thread
+  static constexpr int kBPer = kNarrowSK * kNarrowCols / 64;  // B floats per thread (16)
+  // A is staged row-major ([row][k], rows of kNarrowSK + 4 floats: 16-byte
+  // aligned, and eight consecutive rows start in distinct groups of four
+  // banks, so 16-byte reads of eight lanes do not conflict); B as [k][col].
+  static constexpr int kLdA = kNarrowSK + 4, kLdB = kNarrowCols + PAD, kLdR = kNarrowCols + PAD;
+  static constexpr int kStageFloats = TM * kLdA + kNarrowSK * kLdB;
+  static constexpr int kSmemFloats = kNarrowKG * 2 * kStageFloats;
+  static_assert(TM == 32 || TM == 64, "tile rows");
+  static_assert(kAPer % 4 == 0 && kBPer % 4 == 0, "16-byte staging");
+  static_assert(kNarrowKG * TM * kLdR <= kSmemFloats, "the waves' sums reuse the staging LDS");
+  static_assert(kSmemFloats * 4 <= 160 * 1024, "LDS of one CU");
+};
+
+__device__ __forceinline__ void put4(float* r, int q, float4 v) {
+  r[4 * q] = v.x; r[4 * q + 1] = v.y; r[4 * q + 2] = v.z; r[4 * q + 3] = v.w;
+}
+__device__ __forceinline__ float4 get4(const float* r, int q) {
+  return make_float4(r[4 * q], r[4 * q + 1], r[4 * q + 2], r[4 * q + 3]);
+}
+
+// Global column of B for tile column c (plain: n0 + c; step: k of channel
+// n0 + c for c < 32, p of channel n0 + c - 32 after).
+template <int MODE>
+__device__ __forceinline__ int64_t narrow_col(const GemmParams& P, int64_t n0, int c) {
+  if (MODE == kPlain) return n0 + c;
+  return int64_t(c / 32) * P.D_h + n0 + (c % 32);
+}
+template <int MODE>
+__device__ __forceinline__ bool narrow_col_ok(const GemmParams& P, int64_t n0, int c) {
+  return MODE == kPlain ? n0 + c < P.N : n0 + (c % 32) < P.D_h;
+}
+
+template <int MODE, int TM, bool FULL>
+__global__ __launch_bounds__(64 * kNarrowKG) void narrow_kernel(const GemmParams P) {
+  using G = Narrow<TM>;
+  constexpr int SK = kNarrowSK, KG = kNarrowKG, RI = G::kRI;
+  __shared__ __align__(16) float smem[G::kSmemFloats];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int g = __builtin_amdgcn_readfirstlane(tid >> 6);  // this wave's K group
+  const int kl = lane >> 5, ml = lane & 31;
+  const int64_t cols = MODE == kPlain ? P.N : P.D_h;
+  const int64_t tiles_m = (P.M + TM - 1) / TM;
+  const uint32_t tile = xcd_contiguous(blockIdx.x, gridDim.x);
+  const int64_t m0 = int64_t(tile % uint32_t(tiles_m)) * TM;  // row tiles of a column tile adjacent
+  const int64_t n0 = int64_t(tile / uint32_t(tiles_m)) * (MODE == kPlain ? kNarrowCols : kNarrowCols / 2);
+
+  // This wave's K stages.
+  const int64_t n_kt = (P.K + SK - 1) / SK;
+  const int64_t per = (n_kt + KG - 1) / KG;
+  const int64_t kt0 = g * per;
+  const int64_t kt1 = kt0 + per < n_kt ? kt0 + per : n_kt;
+  const int iters = int(per);  // the same for every wave (shared barriers)
+
+  float* As = smem + g * 2 * G::kStageFloats;  // [2][TM][kLdA]
+  float* Bs = As + TM * G::kLdA;               // [2][SK][kLdB], stage stride kStageFloats
+  auto a_vec4 = [&](int buf, int row, int k) -> float4& {
+    return *reinterpret_cast<float4*>(As + buf * G::kStageFloats + row * G::kLdA + k);
+  };
+  auto b_at = [&](int buf, int k, int c) -> float& { return Bs[buf * G::kStageFloats + k * G::kLdB + c]; };
+
+  // Staging, in float4 chunks.  A chunk q of a lane: row q * 16 + lane / 4,
+  // k (lane % 4) * 4, so one load instruction covers 16 whole row segments
+  // (16 cache lines, not 64).  B chunk q: k row q * 4 + lane / 16, columns
+  // (lane % 16) * 4: four whole 256-byte row segments per instruction.
+  constexpr int kAQ = G::kAPer / 4, kBQ = G::kBPer / 4;
+  static_assert(kAQ * 16 == TM && kBQ * 4 == SK && SK == 16, "staging chunks cover the stage");
+  const int a_r = lane >> 2, a_k = (lane & 3) * 4;
+  const int b_k = lane >> 4, b_c = (lane & 15) * 4;
+  const bool a_vec = (P.lda % 4 == 0) && ((reinterpret_cast<uintptr_t>(P.A) & 15) == 0);
+  const bool b_vec = (P.ldb % 4 == 0) && ((reinterpret_cast<uintptr_t>(P.Bm) & 15) == 0) &&
+                     (MODE == kPlain || P.D_h % 4 == 0);
+  const bool b_cols_ok = narrow_col_ok<MODE>(P, n0, b_c + 3);  // the chunk's last column
+  const int64_t gc = narrow_col<MODE>(P, n0, b_c);
+  float ra[4 * kAQ], rb[4 * kBQ];  // plain floats: kept in registers
+  const float* a_ptr = P.A + (m0 + a_r) * P.lda + kt0 * SK + a_k;
+  const float* b_ptr = P.Bm + (kt0 * SK + b_k) * P.ldb + gc;
+
+  auto load_full = [&]() {
+#pragma unroll
+    for (int q = 0; q < kAQ; ++q) put4(ra, q, *reinterpret_cast<const float4*>(a_ptr + q * 16 * P.lda));
+#pragma unroll
+    for (int q = 0; q < kBQ; ++q) put4(rb, q, *reinterpret_cast<const float4*>(b_ptr + q * 4 * P.ldb));
+    a_ptr += SK;
+    b_ptr += SK * P.ldb;
+  };
+  // K stage kt of this wave (zeros past the wave's range, K, M or N).
+  auto load_checked = [&](int64_t kt) {
+    const bool in = kt < kt1;
+    const int64_t k_lim = in ? (kt + 1) * SK < P.K ? (kt + 1) * SK : P.K : 0;
+    const int64_t ka = kt * SK + a_k;
+#pragma unroll
+    for (int q = 0; q < kAQ; ++q) {
+      const int64_t gm = m0 + q * 16 + a_r;
+      const bool row_ok = gm < P.M;
+      if (row_ok && a_vec && ka + 4 <= k_lim) {
+        put4(ra, q, *reinterpret_cast<const float4*>(P.A + gm * P.lda + ka));
+      } else {
+        float v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = (row_ok && ka + j < k_lim) ? P.A[gm * P.lda + ka + j] : 0.0f;
+        put4(ra, q, make_float4(v[0], v[1], v[2], v[3]));
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kBQ; ++q) {
+      const int64_t kb = kt * SK + q * 4 + b_k;
+      const bool k_ok = kb < k_lim;
+      if (k_ok && b_vec && b_cols_ok) {
+        put4(rb, q, *reinterpret_cast<const float4*>(P.Bm + kb * P.ldb + gc));
+      } else {
+        float v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          v[j] = (k_ok && narrow_col_ok<MODE>(P, n0, b_c + j))
+                     ? P.Bm[kb * P.ldb + narrow_col<MODE>(P, n0, b_c + j)]
+                     : 0.0f;
+        put4(rb, q, make_float4(v[0], v[1], v[2], v[3]));
+      }
+    }
+  };
+  auto store_stage = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < kAQ; ++q) a_vec4(buf, q * 16 + a_r, a_k) = get4(ra, q);
+#pragma unroll
+    for (int q = 0; q < kBQ; ++q)
+      *reinterpret_cast<float4*>(&b_at(buf, q * 4 + b_k, b_c)) = get4(rb, q);
+  };
+
+  // Step mode: thread t finishes the (row, channel) pairs t, t + kThreads,
+  // ... of the tile (channels fastest); their carried states are read now,
+  // so that those loads are not waited for after the K loop.
+  constexpr int kCh = kNarrowCols / 2;
+  constexpr int kPairs = MODE == kStep ? TM * kCh / G::kThreads : 1;
+  float carried[kPairs];
+  if constexpr (MODE == kStep) {
+#pragma unroll
+    for (int q = 0; q < kPairs; ++q) {
+      const int e = tid + q * G::kThreads;
+      const int64_t grow = m0 + e / kCh, d = n0 + e % kCh;
+      carried[q] = (grow < P.M && d < cols) ? carried_state(P, grow, d) : 0.0f;
+    }
+  }
+
+  floatx16 acc[RI][2];
+#pragma unroll
+  for (int i = 0; i < RI; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  if constexpr (FULL) load_full(); else load_checked(kt0);
+  store_stage(0);
+  __syncthreads();
+  for (int it = 0; it < iters; ++it) {
+    const int buf = it & 1;
+    if (it + 1 < iters) {
+      if constexpr (FULL) load_full(); else load_checked(kt0 + it + 1);
+    }
+    // K order within a stage: MFMA s (s < SK / 2) takes k = s from lanes
+    // 0..31 and k = SK / 2 + s from lanes 32..63 (the same for A and B), so a
+    // lane reads its A values of all SK / 2 MFMAs with 16-byte reads.
+    float a[RI][SK / 2];
+#pragma unroll
+    for (int i = 0; i < RI; ++i)
+#pragma unroll
+      for (int q = 0; q < SK / 8; ++q) {
+        const float4 v = a_vec4(buf, i * 32 + ml, kl * (SK / 2) + 4 * q);
+        a[i][4 * q + 0] = v.x; a[i][4 * q + 1] = v.y; a[i][4 * q + 2] = v.z; a[i][4 * q + 3] = v.w;
+      }
+#pragma unroll
+    for (int s = 0; s < SK / 2; ++s) {
+      float b[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) b[j] = b_at(buf, kl * (SK / 2) + s, j * 32 + ml);
+#pragma unroll
+      for (int i = 0; i < RI; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][s], b[j], acc[i][j], 0, 0, 0);
+    }
+    if (it + 1 < iters) store_stage(buf ^ 1);
+    __syncthreads();
+  }
+
+  // The waves' sums: red[g][row][c] over the staging LDS (free after the
+  // loop's last barrier).
+  float* red = smem;
+  constexpr int kRedWave = TM * G::kLdR;
+#pragma unroll
+  for (int i = 0; i < RI; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = i * 32 + (r / 4) * 8 + kl * 4 + (r % 4);
+        red[g * kRedWave + row * G::kLdR + j * 32 + ml] = acc[i][j][r];
+      }
+  __syncthreads();
+  if (MODE == kPlain) {
+    // Thread t: elements t, t + kThreads, ... of the TM x 64 tile (columns fastest).
+#pragma unroll
+    for (int q = 0; q < TM * kNarrowCols / G::kThreads; ++q) {
+      const int e = tid + q * G::kThreads;
+      const int row = e / kNarrowCols, c = e % kNarrowCols;
+      float v = red[row * G::kLdR + c];
+#pragma unroll
+      for (int h = 1; h < KG; ++h) v += red[h * kRedWave + row * G::kLdR + c];
+      const int64_t grow = m0 + row, gcol = n0 + c;
+      if (grow < P.M && gcol < cols) P.C[grow * P.ldc + gcol] = v;
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < kPairs; ++q) {
+      const int e = tid + q * G::kThreads;
+      const int row = e / kCh, c = e % kCh;
+      float k = red[row * G::kLdR + c], p = red[row * G::kLdR + kCh + c];
+#pragma unroll
+      for (int h = 1; h < KG; ++h) {
+        k += red[h * kRedWave + row * G::kLdR + c];
+        p += red[h * kRedWave + row * G::kLdR + kCh + c];
+      }
+      const int64_t grow = m0 + row, d = n0 + c;
+      if (grow < P.M && d < cols) P.h_next[grow * P.D_h + d] = step_value(k, p, carried[q]);
+    }
+  }
+}
+
 // Split-K reductions: the K slices' sums are added in slice order (so the
 // result does not depend on scheduling), then stored or used by the step.
 __global__ void reduce_plain_kernel(const float* part, int S, int64_t M, int64_t N, float* C,
@@ -216,9 +473,10 @@ __global__ void reduce_step_kernel(const GemmParams P, int S) {
 int gemm_splits(int64_t M, int64_t N, int64_t K, bool step) {
   // Enough workgroups for two per CU on a 256-CU part, each K slice at
   // least 256 deep; small problems (the single-token step) split K, large
-  // ones (whole-sequence projections) do not.  Products of at most kSmallM
-  // rows take the FMA path, which splits K inside the workgroup.
-  if (M <= kSmallM) return 1;
+  // ones (whole-sequence projections) do not.  Products of at most
+  // kNarrowMaxM rows take the FMA path or the narrow tiles, which split K
+  // inside the workgroup.
+  if (M <= kNarrowMaxM) return 1;
   const int64_t tiles = ((M + BM - 1) / BM) * (step ? (N / 2 + BN / 2 - 1) / (BN / 2)
                                                     : (N + BN - 1) / BN);
   if (tiles <= 0 || tiles >= 512) return 1;
@@ -267,6 +525,40 @@ hipError_t launch_small_m(const GemmParams& P, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int MODE, int TM>
+void launch_narrow_tm(bool full, uint32_t tiles, const GemmParams& P, hipStream_t stream) {
+  const dim3 grid{tiles}, block{uint32_t(Narrow<TM>::kThreads)};
+  if (full)
+    hipLaunchKernelGGL((narrow_kernel<MODE, TM, true>), grid, block, 0, stream, P);
+  else
+    hipLaunchKernelGGL((narrow_kernel<MODE, TM, false>), grid, block, 0, stream, P);
+}
+
+// 64-row tiles when they alone give about a workgroup per CU, else 32-row
+// tiles (twice as many).
+template <int MODE>
+sr_status launch_narrow(const GemmParams& P, hipStream_t stream) {
+  const int64_t col_tiles = MODE == kPlain ? (P.N + kNarrowCols - 1) / kNarrowCols
+                                           : (P.D_h + kNarrowCols / 2 - 1) / (kNarrowCols / 2);
+  const int64_t tiles64 = ((P.M + 63) / 64) * col_tiles;
+  const int tm = tiles64 >= 192 ? 64 : 32;
+  const int64_t tiles = ((P.M + tm - 1) / tm) * col_tiles;
+  if (tiles > int64_t(0x7FFFFFFF) / 512)
+    return fail(SR_ERR_UNSUPPORTED, "GEMM of %lld narrow tiles too large", (long long)tiles);
+  const auto al16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
+  const bool full = P.K > 0 && P.M % tm == 0 &&
+                    (MODE == kPlain ? P.N % kNarrowCols == 0 : P.D_h % (kNarrowCols / 2) == 0) &&
+                    P.K % (int64_t(kNarrowSK) * kNarrowKG) == 0 && P.lda % 4 == 0 &&
+                    P.ldb % 4 == 0 && al16(P.A) && al16(P.Bm);
+  if (tm == 64)
+    launch_narrow_tm<MODE, 64>(full, uint32_t(tiles), P, stream);
+  else
+    launch_narrow_tm<MODE, 32>(full, uint32_t(tiles), P, stream);
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return fail(SR_ERR_HIP, "narrow GEMM launch: %s", hipGetErrorString(err));
+  return SR_OK;
+}
+
 template <int MODE, int TBM>
 void launch_tiles(bool full, dim3 grid, const GemmParams& P, hipStream_t stream) {
   if (full)
@@ -284,6 +576,7 @@ sr_status launch_mode(int mode, GemmParams P, float* ws, hipStream_t stream) {
     if (e != hipSuccess) return fail(SR_ERR_HIP, "small GEMM launch: %s", hipGetErrorString(e));
     return SR_OK;
   }
+  if (P.M <= kNarrowMaxM) return mode == kPlain ? launch_narrow<kPlain>(P, stream) : launch_narrow<kStep>(P, stream);
   const int64_t cols_per_tile = mode == kPlain ? BN : BN / 2;
   const int64_t n_cols = mode == kPlain ? P.N : P.D_h;
   P.tiles_n = (n_cols + cols_per_tile - 1) / cols_per_tile;

@@ -56,9 +56,12 @@ def test_workspace_sizes():
     assert all(v % 256 == 0 for v in (s0, s1, s2, small))
     assert lib.minmax_scan_workspace_size(8, 32768, 192) > 0
     assert lib.mingru_forward_workspace_size(-1, 4, 4, 4, 4, 0, 0) == 0
-    # The single-token step splits K for small batches: its partial sums
-    # need workspace; tiny shapes need none.
-    assert lib.mingru_step_workspace_size(256, 2048, 2048, 2048) >= 256 * 4096 * 4 * 2
+    # The single-token step splits K inside the workgroup up to 512 streams
+    # (no workspace); larger batches split it across workgroups, whose
+    # partial sums need workspace; tiny shapes need none.
+    assert lib.mingru_step_workspace_size(256, 2048, 2048, 2048) == 0
+    assert lib.mingru_step_workspace_size(512, 2048, 2048, 2048) == 0
+    assert lib.mingru_step_workspace_size(1024, 2048, 2048, 2048) >= 1024 * 4096 * 4 * 2
     assert lib.mingru_step_workspace_size(2, 4, 4, 4) == 0
 
 
@@ -97,10 +100,11 @@ def test_forward_rejects_bad_arguments(kw, code):
 
 def test_step_rejects_bad_arguments():
     f = lib.mingru_step
-    need = lib.mingru_step_workspace_size(256, 2048, 2048, 2048)
-    assert f(256, 2048, 2048, 2048, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, 0,
+    need = lib.mingru_step_workspace_size(1024, 2048, 2048, 2048)  # K split across workgroups
+    assert need > 0
+    assert f(1024, 2048, 2048, 2048, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, 0,
              None) == sr.SR_ERR_INVALID_ARGUMENT
-    assert f(256, 2048, 2048, 2048, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, need - 1,
+    assert f(1024, 2048, 2048, 2048, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, need - 1,
              None) == sr.SR_ERR_WORKSPACE_TOO_SMALL
     assert f(-1, 4, 4, 4, FAKE, FAKE, None, None, FAKE, None, None, 0, None) == sr.SR_ERR_INVALID_ARGUMENT
     assert f(2, 4, 4, 4, FAKE, None, None, None, FAKE, None, None, 0, None) == sr.SR_ERR_INVALID_ARGUMENT
@@ -160,8 +164,8 @@ def test_forward_decayed_rejects_bad_arguments(kw, code):
 
 def test_step_decayed_rejects_bad_arguments():
     f = lib.mingru_step_decayed
-    need = lib.mingru_step_workspace_size(256, 2048, 2048, 2048)
-    args = [256, 2048, 2048, 2048, FAKE, FAKE, FAKE]
+    need = lib.mingru_step_workspace_size(1024, 2048, 2048, 2048)
+    args = [1024, 2048, 2048, 2048, FAKE, FAKE, FAKE]
     tail = [FAKE, FAKE, FAKE, FAKE, need - 1, None]   # h_prev, h_next, y_t, ws, bytes, stream
     assert f(*args, None, FAKE, 0, None, *tail) == sr.SR_ERR_INVALID_ARGUMENT
     assert f(*args, FAKE, None, 0, None, *tail) == sr.SR_ERR_INVALID_ARGUMENT
