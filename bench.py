@@ -23,8 +23,8 @@ carries:
                 --cpu-steps takes a prefix);
 * legs       -- the other measurements: the MinMax scan, the backward passes
                 of both scans, the time-decayed scan, the decode-style step
-                loop with its prefill, the small layers, and a device copy
-                ceiling.
+                loop with its prefill, the small layers, the MinMax token
+                loop, and a device copy ceiling.
 
 Only one GPU is used; --gpus above 1 exits with a message.
 """
@@ -167,6 +167,55 @@ def leg_minmax(torch, sr, synth, steps, warmup):
     return dict(B=B, T=T, D=D, elements_per_s=n / (wall / steps), launch_ms_mean=mean_ms,
                 achieved_GBps=alg / (mean_ms * 1e-3) / 1e9,
                 frac_of_hbm_peak=alg / (mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS)
+
+
+def leg_minmax_step(torch, sr, synth, n_steps):
+    """The MinMax neuron one token at a time at the MinMax workload's width
+    (B=8, D=192), in place: eagerly and replayed from a HIP graph.  The final
+    state is checked bit for bit against the scan over the same tokens."""
+    cfg = synth.CONFIGS[5]
+    B, D = cfg["B"], cfg["D"]
+    r = synth.device_uniform(5, "r", (B, n_steps, D), -1.0, 1.0)
+    s = synth.device_uniform(5, "s", (B, n_steps, D), -1.5, 0.5)
+    x0 = synth.device_uniform(5, "x0", (B, D), -1.0, 1.0)
+    rs = [r[:, t].contiguous() for t in range(n_steps)]
+    ss = [s[:, t].contiguous() for t in range(n_steps)]
+    x = torch.empty_like(x0)
+
+    def loop():
+        x.copy_(x0)
+        for t in range(n_steps):
+            sr.minmax_step(rs[t], ss[t], x, x_next=x)
+
+    loop()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    loop()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    _, last = sr.minmax_scan(r, s, x0, return_last=True)
+    exact = bool(torch.equal(x, last))
+    res = dict(B=B, D=D, steps=n_steps, step_loop_ms=dt * 1e3, steps_per_s=n_steps / dt,
+               matches_scan_bitwise=exact)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        loop()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        loop()
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g.replay()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    res["graph_step_loop_ms"] = dt * 1e3
+    res["graph_steps_per_s"] = n_steps / dt
+    res["graph_matches_scan_bitwise"] = bool(torch.equal(x, last))
+    del g
+    return res
 
 
 def leg_scan_backward(torch, sr, synth, steps, warmup):
@@ -352,7 +401,8 @@ def main():
     # A fresh process reaches steady clocks only after a few hundred ms of
     # sustained load (measured: the first ~100 launches run 3-5% slower).
     ap.add_argument("--warmup", type=int, default=1000)
-    ap.add_argument("--legs", default="scan,minmax,scan_bwd,minmax_bwd,scan_decay,decode,layer_d512,layer_d16,copy")
+    ap.add_argument("--legs", default="scan,minmax,scan_bwd,minmax_bwd,scan_decay,decode,layer_d512,"
+                                      "layer_d16,minmax_step,copy")
     ap.add_argument("--cpu-steps", type=int, default=65536,
                     help="sequence prefix the CPU oracle baseline runs over (0 = skip)")
     ap.add_argument("--decode-steps", type=int, default=4096)
@@ -393,6 +443,8 @@ def main():
         extra["layer_b2_t64_d16"] = leg_layer(torch, sr, synth, 1, 10)
     if "decode" in legs:
         extra["step_b256_d2048"] = leg_decode(torch, sr, synth, args.decode_steps)
+    if "minmax_step" in legs:
+        extra["minmax_step_b8_d192"] = leg_minmax_step(torch, sr, synth, 4096)
     if head is not None:
         out.update({
             "value": head["value"], "unit": "elements/s", "n_gpus": 1, "steps": args.steps,
