@@ -143,6 +143,24 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+_stand_ins = {}
+
+
+def _operand(t):
+    """Pointer of an optional weight that is present.  The C calls read NULL
+    as "absent" (no projection), so a present weight with no elements (D_in
+    or D_h of 0), whose tensor has no storage, is passed as a valid non-NULL
+    address that the library never dereferences."""
+    if t is None:
+        return None
+    if t.numel() > 0:
+        return ctypes.c_void_p(t.data_ptr())
+    dev = t.device
+    if dev not in _stand_ins:
+        _stand_ins[dev] = torch.zeros(4, dtype=torch.float32, device=dev)
+    return ctypes.c_void_p(_stand_ins[dev].data_ptr())
+
+
 def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
@@ -282,16 +300,16 @@ def _forward(x, W_in, k, p, h0, W_out, return_last, workspace, out, out_last, de
     ws = _use_workspace(workspace, nbytes, device)
     if decay is None:
         st = _lib.mingru_forward(B, T, D_in, D_h, D_out, _ptr(x if W_in is not None else None),
-                                 _ptr(W_in), _ptr(kk), _ptr(pp), ld_kp, kp_dtype, _ptr(h0),
-                                 _ptr(W_out), _ptr(y), _ptr(h_last), _ptr(ws), ws.numel(),
+                                 _operand(W_in), _ptr(kk), _ptr(pp), ld_kp, kp_dtype, _ptr(h0),
+                                 _operand(W_out), _ptr(y), _ptr(h_last), _ptr(ws), ws.numel(),
                                  _stream(device))
         _check("mingru_forward", st)
     else:
         rate, gap, log1p, sat = _decay_args(decay, D_h, (B, T), device)
         st = _lib.mingru_forward_decayed(B, T, D_in, D_h, D_out,
-                                         _ptr(x if W_in is not None else None), _ptr(W_in),
+                                         _ptr(x if W_in is not None else None), _operand(W_in),
                                          _ptr(kk), _ptr(pp), ld_kp, kp_dtype, _ptr(rate),
-                                         _ptr(gap), log1p, _ptr(sat), _ptr(h0), _ptr(W_out),
+                                         _ptr(gap), log1p, _ptr(sat), _ptr(h0), _operand(W_out),
                                          _ptr(y), _ptr(h_last), _ptr(ws), ws.numel(),
                                          _stream(device))
         _check("mingru_forward_decayed", st)
@@ -348,13 +366,13 @@ def _step(x_t, W_in, W_out, h_prev, h_next, workspace, decay):
     if nbytes:
         ws = _use_workspace(workspace, nbytes, device)
     if decay is None:
-        st = _lib.mingru_step(B, D_in, D_h, D_out, _ptr(x_t), _ptr(W_in), _ptr(W_out),
+        st = _lib.mingru_step(B, D_in, D_h, D_out, _ptr(x_t), _operand(W_in), _operand(W_out),
                               _ptr(h_prev), _ptr(h_next), _ptr(y_t), _ptr(ws),
                               0 if ws is None else ws.numel(), _stream(device))
         _check("mingru_step", st)
     else:
         rate, gap, log1p, sat = _decay_args(decay, D_h, (B,), device)
-        st = _lib.mingru_step_decayed(B, D_in, D_h, D_out, _ptr(x_t), _ptr(W_in), _ptr(W_out),
+        st = _lib.mingru_step_decayed(B, D_in, D_h, D_out, _ptr(x_t), _operand(W_in), _operand(W_out),
                                       _ptr(rate), _ptr(gap), log1p, _ptr(sat), _ptr(h_prev),
                                       _ptr(h_next), _ptr(y_t), _ptr(ws),
                                       0 if ws is None else ws.numel(), _stream(device))

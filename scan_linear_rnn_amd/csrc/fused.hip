@@ -207,10 +207,12 @@ sr_status launch_fused_forward(const FusedRequest& rq) {
   const size_t used = eng::kHeaderBytes + size_t(P.n_tchunks) * size_t(rq.B) * size_t(rq.D_h) * 8;
   sr_status st = eng::reset_workspace(ws, used, rq.stream);
   if (st != SR_OK) return st;
-  // Every tile full (whole 256-step tiles, whole channel tiles, K in steps
-  // of 16) with 16-byte operands: the K loop needs no range tests.
+  // Every tile full (whole 256-step tiles, whole channel tiles, K a
+  // positive multiple of 16) with 16-byte operands: the K loop needs no range
+  // tests.  (It loads its first K step unconditionally, so K = 0, where x may
+  // be NULL, takes the checked loop.)
   const auto al16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
-  const bool full = rq.T % kTileT == 0 && rq.D_h % kTileD == 0 && rq.D_in % BK == 0 &&
+  const bool full = rq.D_in > 0 && rq.T % kTileT == 0 && rq.D_h % kTileD == 0 && rq.D_in % BK == 0 &&
                     rq.D_in % 4 == 0 && al16(rq.x) && al16(rq.W_in);
   const dim3 grid{uint32_t(tiles)}, block{2 * kTileT};
   if (rq.decay_rate != nullptr && full)

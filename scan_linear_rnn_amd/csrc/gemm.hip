@@ -476,7 +476,7 @@ int gemm_splits(int64_t M, int64_t N, int64_t K, bool step) {
   // ones (whole-sequence projections) do not.  Products of at most
   // kNarrowMaxM rows take the FMA path or the narrow tiles, which split K
   // inside the workgroup.
-  if (M <= kNarrowMaxM) return 1;
+  if (M <= kNarrowMaxM || K < 2 * 256) return 1;  // nothing worth splitting (and K = 0 has no slices)
   const int64_t tiles = ((M + BM - 1) / BM) * (step ? (N / 2 + BN / 2 - 1) / (BN / 2)
                                                     : (N + BN - 1) / BN);
   if (tiles <= 0 || tiles >= 512) return 1;
@@ -597,7 +597,7 @@ sr_status launch_mode(int mode, GemmParams P, float* ws, hipStream_t stream) {
   // Every tile full (rows, columns, whole K steps in every slice) and
   // 16-byte operands: the loads need no range tests.
   const auto al16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
-  const bool full = P.M % tbm == 0 && n_cols % cols_per_tile == 0 && P.K % BK == 0 &&
+  const bool full = P.K > 0 && P.M % tbm == 0 && n_cols % cols_per_tile == 0 && P.K % BK == 0 &&
                     P.k_split % BK == 0 && P.K % P.k_split == 0 && P.lda % 4 == 0 &&
                     P.ldb % 4 == 0 && al16(P.A) && al16(P.Bm) && (mode == kPlain || P.D_h % 4 == 0);
   if (mode == kPlain && big)

@@ -65,6 +65,28 @@ def test_workspace_sizes():
     assert lib.mingru_step_workspace_size(2, 4, 4, 4) == 0
 
 
+def test_workspace_sizes_with_zero_and_small_dims():
+    """Every size query over grids that include zero dimensions (no input
+    features, no state, no output, empty batch or sequence) returns without
+    faulting, and K = 0 never asks for split-K partial sums."""
+    import itertools
+    for B, T, D_in, D_h, D_out in itertools.product([0, 1, 4, 600], [0, 1, 1000], [0, 1, 700],
+                                                    [0, 1, 256], [0, 5]):
+        for w_in, w_out in itertools.product([0, 1], [0, 1]):
+            n = lib.mingru_forward_workspace_size(B, T, D_in, D_h, D_out, w_in, w_out)
+            assert n % 256 == 0
+        assert lib.mingru_step_workspace_size(B, D_in, D_h, D_out) >= 0
+        assert lib.minmax_scan_workspace_size(B, T, D_h) >= 0
+        assert lib.mingru_scan_backward_workspace_size(B, T, D_h) >= 0
+    # No input features: the input product has K = 0 and needs no partial
+    # sums (with K = 1024 it splits); D_out = 0 leaves no output product.
+    assert lib.mingru_step_workspace_size(1024, 0, 512, 0) == 0
+    assert lib.mingru_step_workspace_size(1024, 1024, 512, 0) > 0
+    plain = lib.mingru_forward_workspace_size(4, 1000, 0, 256, 256, 1, 0)
+    staged = 4 * 1000 * 2 * 256 * 4   # the [k|p] staging alone
+    assert staged <= plain < staged + (1 << 20)
+
+
 def _fwd(**kw):
     args = dict(B=2, T=8, D_in=0, D_h=4, D_out=4, x=None, W_in=None, k=FAKE, p=FAKE2,
                 ld_kp=4, kp_dtype=sr.SR_F32, h0=None, W_out=None, y=FAKE, h_last=None,
