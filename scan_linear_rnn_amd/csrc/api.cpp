@@ -144,59 +144,72 @@ sr_status forward_impl(int64_t B, int64_t T, int64_t D_in, int64_t D_h, int64_t 
     if (w_out && n_y > 0) return launch_copy_or_zero(y, nullptr, n_y, s);
     return SR_OK;
   }
-  if (w_in && T > 0 && fused_forward_applies(B, T, D_h)) {
-    FusedRequest fr{};
-    fr.B = B;
-    fr.T = T;
-    fr.D_in = D_in;
-    fr.D_h = D_h;
-    fr.x = x;
-    fr.W_in = W_in;
-    fr.h0 = h0;
-    fr.h = h_buf;
-    fr.h_last = h_last;
-    fr.workspace = ws;
-    fr.stream = s;
-    if (dec != nullptr) {
-      fr.decay_rate = dec->rate;
-      fr.delta_t = dec->delta_t;
-      fr.log1p_delta = dec->log1p_delta;
-      fr.saturated = dec->saturated;
+  // The launches of the call; run once with check_only (every launch's own
+  // checks, nothing enqueued), then for real, so that a failing check never
+  // leaves earlier launches behind.
+  const bool fused = w_in && T > 0 && fused_forward_applies(B, T, D_h);
+  auto run = [&](bool check_only) -> sr_status {
+    sr_status st2;
+    if (fused) {
+      FusedRequest fr{};
+      fr.B = B;
+      fr.T = T;
+      fr.D_in = D_in;
+      fr.D_h = D_h;
+      fr.x = x;
+      fr.W_in = W_in;
+      fr.h0 = h0;
+      fr.h = h_buf;
+      fr.h_last = h_last;
+      fr.workspace = ws;
+      fr.stream = s;
+      if (dec != nullptr) {
+        fr.decay_rate = dec->rate;
+        fr.delta_t = dec->delta_t;
+        fr.log1p_delta = dec->log1p_delta;
+        fr.saturated = dec->saturated;
+      }
+      fr.check_only = check_only;
+      st2 = launch_fused_forward(fr);
+      if (st2 != SR_OK || !w_out) return st2;
+      return launch_gemm_f32(B * T, D_out, D_h, h_buf, D_h, W_out, D_out, y, D_out, g_buf, s,
+                             check_only);
     }
-    st = launch_fused_forward(fr);
-    if (st != SR_OK) return st;
-    if (w_out) st = launch_gemm_f32(B * T, D_out, D_h, h_buf, D_h, W_out, D_out, y, D_out, g_buf, s);
-    return st;
-  }
-  if (w_in && T > 0) {
-    st = launch_gemm_f32(B * T, 2 * D_h, D_in, x, D_in, W_in, 2 * D_h, kp_buf, 2 * D_h, g_buf, s);
-    if (st != SR_OK) return st;
-  }
-  ScanRequest rq{};
-  rq.op = ScanOp::kMinGRU;
-  rq.in_dtype = w_in ? SR_F32 : kp_dtype;
-  rq.B = B;
-  rq.T = T;
-  rq.D = D_h;
-  rq.in0 = w_in ? static_cast<const void*>(kp_buf) : k;
-  rq.in1 = w_in ? static_cast<const void*>(kp_buf + D_h) : p;
-  rq.ld_in = w_in ? 2 * D_h : ld_kp;
-  rq.init = h0;
-  rq.out = h_buf;
-  rq.last = h_last;
-  rq.workspace = ws;
-  rq.stream = s;
-  if (dec != nullptr) {
-    rq.decay_rate = dec->rate;
-    rq.delta_t = dec->delta_t;
-    rq.log1p_delta = dec->log1p_delta;
-    rq.saturated = dec->saturated;
-  }
-  st = launch_scan(rq);
-  if (st != SR_OK) return st;
-  if (w_out && T > 0)
-    st = launch_gemm_f32(B * T, D_out, D_h, h_buf, D_h, W_out, D_out, y, D_out, g_buf, s);
-  return st;
+    if (w_in && T > 0) {
+      st2 = launch_gemm_f32(B * T, 2 * D_h, D_in, x, D_in, W_in, 2 * D_h, kp_buf, 2 * D_h, g_buf, s,
+                            check_only);
+      if (st2 != SR_OK) return st2;
+    }
+    ScanRequest rq{};
+    rq.op = ScanOp::kMinGRU;
+    rq.in_dtype = w_in ? SR_F32 : kp_dtype;
+    rq.B = B;
+    rq.T = T;
+    rq.D = D_h;
+    rq.in0 = w_in ? static_cast<const void*>(kp_buf) : k;
+    rq.in1 = w_in ? static_cast<const void*>(kp_buf + D_h) : p;
+    rq.ld_in = w_in ? 2 * D_h : ld_kp;
+    rq.init = h0;
+    rq.out = h_buf;
+    rq.last = h_last;
+    rq.workspace = ws;
+    rq.stream = s;
+    if (dec != nullptr) {
+      rq.decay_rate = dec->rate;
+      rq.delta_t = dec->delta_t;
+      rq.log1p_delta = dec->log1p_delta;
+      rq.saturated = dec->saturated;
+    }
+    rq.check_only = check_only;
+    st2 = launch_scan(rq);
+    if (st2 != SR_OK) return st2;
+    if (w_out && T > 0)
+      st2 = launch_gemm_f32(B * T, D_out, D_h, h_buf, D_h, W_out, D_out, y, D_out, g_buf, s,
+                            check_only);
+    return st2;
+  };
+  st = run(true);
+  return st != SR_OK ? st : run(false);
 }
 
 sr_status step_impl(int64_t B, int64_t D_in, int64_t D_h, int64_t D_out, const float* x_t,
@@ -232,13 +245,19 @@ sr_status step_impl(int64_t B, int64_t D_in, int64_t D_h, int64_t D_out, const f
   float* g_buf = static_cast<float*>(workspace);
   StepDecay sd{};
   if (dec != nullptr) sd = StepDecay{dec->rate, dec->delta_t, dec->log1p_delta, dec->saturated};
-  st = launch_step_in(B, D_in, D_h, x_t, W_in, h_prev, h_next, g_buf, s,
-                      dec != nullptr ? &sd : nullptr);
-  if (st != SR_OK) return st;
-  if (W_out != nullptr)
-    return launch_gemm_f32(B, D_out, D_h, h_next, D_h, W_out, D_out, y_t, D_out, g_buf, s);
-  if (y_t != nullptr && y_t != h_next) return launch_copy_or_zero(y_t, h_next, n_h, s);
-  return SR_OK;
+  // Checked first, then launched (as in forward_impl).
+  auto run = [&](bool check_only) -> sr_status {
+    sr_status st2 = launch_step_in(B, D_in, D_h, x_t, W_in, h_prev, h_next, g_buf, s,
+                                   dec != nullptr ? &sd : nullptr, check_only);
+    if (st2 != SR_OK) return st2;
+    if (W_out != nullptr)
+      return launch_gemm_f32(B, D_out, D_h, h_next, D_h, W_out, D_out, y_t, D_out, g_buf, s,
+                             check_only);
+    if (y_t != nullptr && y_t != h_next && !check_only) return launch_copy_or_zero(y_t, h_next, n_h, s);
+    return SR_OK;
+  };
+  st = run(true);
+  return st != SR_OK ? st : run(false);
 }
 
 }  // namespace

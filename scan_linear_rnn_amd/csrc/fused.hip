@@ -175,6 +175,9 @@ size_t fused_workspace_bytes(int64_t B, int64_t T, int64_t D_h) {
 }
 
 sr_status launch_fused_forward(const FusedRequest& rq) {
+  // fused_forward_applies has checked the grid; nothing else can fail before
+  // the launch.
+  if (rq.check_only) return SR_OK;
   FusedParams F{};
   GemmParams& g = F.g;
   g.M = rq.B * rq.T;

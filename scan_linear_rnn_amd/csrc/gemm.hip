@@ -537,7 +537,7 @@ void launch_narrow_tm(bool full, uint32_t tiles, const GemmParams& P, hipStream_
 // 64-row tiles when they alone give about a workgroup per CU, else 32-row
 // tiles (twice as many).
 template <int MODE>
-sr_status launch_narrow(const GemmParams& P, hipStream_t stream) {
+sr_status launch_narrow(const GemmParams& P, hipStream_t stream, bool check_only) {
   const int64_t col_tiles = MODE == kPlain ? (P.N + kNarrowCols - 1) / kNarrowCols
                                            : (P.D_h + kNarrowCols / 2 - 1) / (kNarrowCols / 2);
   const int64_t tiles64 = ((P.M + 63) / 64) * col_tiles;
@@ -545,6 +545,7 @@ sr_status launch_narrow(const GemmParams& P, hipStream_t stream) {
   const int64_t tiles = ((P.M + tm - 1) / tm) * col_tiles;
   if (tiles > int64_t(0x7FFFFFFF) / 512)
     return fail(SR_ERR_UNSUPPORTED, "GEMM of %lld narrow tiles too large", (long long)tiles);
+  if (check_only) return SR_OK;
   const auto al16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
   const bool full = P.K > 0 && P.M % tm == 0 &&
                     (MODE == kPlain ? P.N % kNarrowCols == 0 : P.D_h % (kNarrowCols / 2) == 0) &&
@@ -567,16 +568,19 @@ void launch_tiles(bool full, dim3 grid, const GemmParams& P, hipStream_t stream)
     hipLaunchKernelGGL((gemm_f32_kernel<MODE, TBM, false>), grid, dim3(2 * TBM), 0, stream, P);
 }
 
-sr_status launch_mode(int mode, GemmParams P, float* ws, hipStream_t stream) {
+sr_status launch_mode(int mode, GemmParams P, float* ws, hipStream_t stream, bool check_only) {
   if (P.M <= kSmallM) {
     if (P.M > 0 && (mode == kPlain ? P.N : P.D_h) > int64_t(0x7FFFFFFF) * 32)
       return fail(SR_ERR_UNSUPPORTED, "GEMM too wide");
+    if (check_only) return SR_OK;
     const hipError_t e = mode == kPlain ? launch_small_m<kPlain>(P, stream)
                                         : launch_small_m<kStep>(P, stream);
     if (e != hipSuccess) return fail(SR_ERR_HIP, "small GEMM launch: %s", hipGetErrorString(e));
     return SR_OK;
   }
-  if (P.M <= kNarrowMaxM) return mode == kPlain ? launch_narrow<kPlain>(P, stream) : launch_narrow<kStep>(P, stream);
+  if (P.M <= kNarrowMaxM)
+    return mode == kPlain ? launch_narrow<kPlain>(P, stream, check_only)
+                          : launch_narrow<kStep>(P, stream, check_only);
   const int64_t cols_per_tile = mode == kPlain ? BN : BN / 2;
   const int64_t n_cols = mode == kPlain ? P.N : P.D_h;
   P.tiles_n = (n_cols + cols_per_tile - 1) / cols_per_tile;
@@ -593,6 +597,7 @@ sr_status launch_mode(int mode, GemmParams P, float* ws, hipStream_t stream) {
   const int64_t tiles = ((P.M + tbm - 1) / tbm) * P.tiles_n;
   if (tiles > 0x7FFFFFFF / (2 * tbm))
     return fail(SR_ERR_UNSUPPORTED, "GEMM of %lld tiles too large", (long long)tiles);
+  if (check_only) return SR_OK;
   const dim3 grid{uint32_t(tiles), 1, uint32_t(S)};
   // Every tile full (rows, columns, whole K steps in every slice) and
   // 16-byte operands: the loads need no range tests.
@@ -626,18 +631,18 @@ sr_status launch_mode(int mode, GemmParams P, float* ws, hipStream_t stream) {
 
 sr_status launch_gemm_f32(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
                           const float* Bm, int64_t ldb, float* C, int64_t ldc, float* ws,
-                          hipStream_t stream) {
+                          hipStream_t stream, bool check_only) {
   if (M == 0 || N == 0) return SR_OK;
   GemmParams P{};
   P.M = M; P.N = N; P.K = K;
   P.A = A; P.lda = lda; P.Bm = Bm; P.ldb = ldb; P.C = C; P.ldc = ldc;
   P.ncols = N;
-  return launch_mode(kPlain, P, ws, stream);
+  return launch_mode(kPlain, P, ws, stream, check_only);
 }
 
 sr_status launch_step_in(int64_t Bsz, int64_t D_in, int64_t D_h, const float* x_t,
                          const float* W_in, const float* h_prev, float* h_next, float* ws,
-                         hipStream_t stream, const StepDecay* decay) {
+                         hipStream_t stream, const StepDecay* decay, bool check_only) {
   if (Bsz == 0 || D_h == 0) return SR_OK;
   GemmParams P{};
   P.M = Bsz; P.N = 2 * D_h; P.K = D_in;
@@ -650,7 +655,7 @@ sr_status launch_step_in(int64_t Bsz, int64_t D_in, int64_t D_h, const float* x_
     P.saturated = decay->saturated;
   }
   P.ncols = 2 * D_h;
-  return launch_mode(kStep, P, ws, stream);
+  return launch_mode(kStep, P, ws, stream, check_only);
 }
 
 }  // namespace sr

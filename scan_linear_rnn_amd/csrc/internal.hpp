@@ -55,6 +55,9 @@ struct ScanRequest {
   const float* delta_t = nullptr;     // [B,T], contiguous
   int log1p_delta = 0;
   uint32_t* saturated = nullptr;      // device flag, OR-ed with 1 on saturation
+  // Run every check the launch makes, then return without enqueuing
+  // anything (so that a call of several launches can check them all first).
+  bool check_only = false;
 };
 
 sr_status launch_scan(const ScanRequest& rq);
@@ -79,6 +82,7 @@ struct FusedRequest {
   const float* delta_t = nullptr;
   int log1p_delta = 0;
   uint32_t* saturated = nullptr;
+  bool check_only = false;  // as in ScanRequest
 };
 
 bool fused_forward_applies(int64_t B, int64_t T, int64_t D_h);
@@ -112,10 +116,12 @@ size_t scan_backward_workspace_bytes(int64_t B, int64_t T, int64_t D);
 // C[M,N] = A[M,K] * B[K,N], fp32, row-major with leading dimensions.  Small
 // problems split K across workgroups; `ws` must then hold
 // gemm_workspace_bytes(M, N, K, false) bytes (it may be null when that is 0).
+// With check_only, every check is made and nothing is enqueued.
 sr_status launch_gemm_f32(int64_t M, int64_t N, int64_t K,
                           const float* A, int64_t lda,
                           const float* Bm, int64_t ldb,
-                          float* C, int64_t ldc, float* ws, hipStream_t stream);
+                          float* C, int64_t ldc, float* ws, hipStream_t stream,
+                          bool check_only = false);
 
 // Time decay of the carried state in the step (see mingru_step_decayed).
 struct StepDecay {
@@ -131,7 +137,7 @@ struct StepDecay {
 sr_status launch_step_in(int64_t Bsz, int64_t D_in, int64_t D_h,
                          const float* x_t, const float* W_in,
                          const float* h_prev, float* h_next, float* ws, hipStream_t stream,
-                         const StepDecay* decay = nullptr);
+                         const StepDecay* decay = nullptr, bool check_only = false);
 
 // Number of K slices a GEMM of this shape uses, and the workspace they need.
 int gemm_splits(int64_t M, int64_t N, int64_t K, bool step);

@@ -307,7 +307,8 @@ sr_status launch_minmax_step(const float* r, const float* s, const float* x_prev
 sr_status launch_scan(const ScanRequest& rq) {
   if (rq.B == 0 || rq.D == 0) return SR_OK;
   if (rq.T == 0) {
-    if (rq.last != nullptr) return launch_copy_or_zero(rq.last, rq.init, rq.B * rq.D, rq.stream);
+    if (rq.last != nullptr && !rq.check_only)
+      return launch_copy_or_zero(rq.last, rq.init, rq.B * rq.D, rq.stream);
     return SR_OK;
   }
   const ScanGeometry g = choose_geometry(rq);
@@ -328,6 +329,7 @@ sr_status launch_scan(const ScanRequest& rq) {
   if (P.n_chains * P.n_tchunks * (64 * kWaves) > int64_t(0xFFFFFFFFu))
     return fail(SR_ERR_UNSUPPORTED, "scan of %lld tiles exceeds one launch's grid",
                 (long long)(P.n_chains * P.n_tchunks));
+  if (rq.check_only) return SR_OK;
   char* ws = static_cast<char*>(rq.workspace);
   P.counter = reinterpret_cast<uint32_t*>(ws);
   P.status = reinterpret_cast<uint32_t*>(ws) + 1;

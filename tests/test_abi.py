@@ -120,6 +120,18 @@ def test_forward_rejects_bad_arguments(kw, code):
     assert lib.scanrnn_last_error()
 
 
+def test_oversized_later_launch_is_rejected_before_any_launch():
+    """A scan-only forward whose scan fits one launch but whose output
+    product's grid does not: the status is SR_ERR_UNSUPPORTED from the check
+    pass, before the scan is enqueued (on this GPU-less host an attempted
+    launch would report SR_ERR_HIP instead)."""
+    B, T, D_h, D_out = 1, 262144, 1, 1 << 20
+    st = _fwd(B=B, T=T, D_in=0, D_h=D_h, D_out=D_out, k=FAKE, p=FAKE2, ld_kp=1,
+              W_out=FAKE, y=FAKE, ws=FAKE, ws_bytes=1 << 40)
+    assert st == sr.SR_ERR_UNSUPPORTED, lib.scanrnn_last_error()
+    assert b"tiles too large" in lib.scanrnn_last_error()
+
+
 def test_step_rejects_bad_arguments():
     f = lib.mingru_step
     need = lib.mingru_step_workspace_size(1024, 2048, 2048, 2048)  # K split across workgroups
