@@ -170,3 +170,35 @@ def test_caller_workspace_is_checked():
         sr.mingru_forward(k=k, p=k, workspace=torch.empty(n, device="cuda"))
     with pytest.raises(ValueError):
         sr.minmax_scan(k, k, torch.zeros((2, 64), device="cuda"), workspace=good[:16])
+
+
+def test_one_workspace_reused_across_shapes_and_ops():
+    """One caller workspace serves a run of calls of different shapes, input
+    types and operators (the scan's look-back words, the MinMax scan's, the
+    backward's) in one stream: every call resets what it uses, so no earlier
+    call's words leak into a later one."""
+    from oracle import minmax
+    lib = sr.raw_library()
+    shapes = [(2, 4096, 512), (3, 1000, 200), (1, 7000, 64), (2, 4096, 512), (4, 300, 1030)]
+    n = max(max(lib.mingru_forward_workspace_size(B, T, 0, D, D, 0, 0),
+                lib.minmax_scan_workspace_size(B, T, D),
+                lib.mingru_scan_backward_workspace_size(B, T, D)) for B, T, D in shapes)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    for i, (B, T, D) in enumerate(shapes):
+        say(f"reuse {i}: B={B} T={T} D={D}")
+        k, p, h0 = _inputs(B, T, D, seed=900 + i)
+        bf16 = i % 2 == 1
+        kd = dev(k).to(torch.bfloat16) if bf16 else dev(k)
+        pd = dev(p).to(torch.bfloat16) if bf16 else dev(p)
+        h = sr.mingru_forward(k=kd, p=pd, h0=dev(h0), workspace=ws)
+        kk, pp = (host64(kd), host64(pd)) if bf16 else (k, p)
+        err = scan_err(host64(h), kk, pp, h0)
+        assert err < (TOL_BF16 if bf16 else TOL_F32), (i, err)
+        rng = np.random.default_rng([901, i])
+        r = rng.uniform(-1, 1, (B, T, D)).astype(np.float32)
+        s = rng.uniform(-1.5, 0.5, (B, T, D)).astype(np.float32)
+        x0 = rng.uniform(-1, 1, (B, D)).astype(np.float32)
+        x = sr.minmax_scan(dev(r), dev(s), dev(x0), workspace=ws)
+        assert np.array_equal(host64(x), minmax.scan(r, s, x0)[0]), i
+        # A backward call between forwards leaves its own words behind.
+        sr.mingru_scan_backward(kd, pd, h, torch.ones_like(h), workspace=ws)
