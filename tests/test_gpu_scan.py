@@ -202,3 +202,61 @@ def test_one_workspace_reused_across_shapes_and_ops():
         assert np.array_equal(host64(x), minmax.scan(r, s, x0)[0]), i
         # A backward call between forwards leaves its own words behind.
         sr.mingru_scan_backward(kd, pd, h, torch.ones_like(h), workspace=ws)
+
+
+def test_chain_of_seven_thousand_tiles_closed_form():
+    """T = 2^20 + 5 in one chain per (batch row, channel tile): the state
+    crosses ~7300 tiles through the look-back.  With k and p constant per
+    channel the recurrence has the closed form h_t = a^t h_0 + b (1 - a^t) /
+    (1 - a), a = sigma(-k), b = sigma(k) g(p) (geometric series), checked in
+    fp64 at sampled steps, every channel.  D = 130: a ragged channel tile.
+    Memory lengths up to ~400 steps (k >= -6): near the fixed point b / c
+    (c = 1 - a) any fp32 evaluation is off by about ulp / c relative, since
+    a itself is held to an ulp (k = -8, c = 3.4e-4, gives ~1.4e-4)."""
+    B, T, D = 2, (1 << 20) + 5, 130
+    say(f"closed form B={B} T={T} D={D}")
+    rng = np.random.default_rng(81)
+    kc = rng.uniform(-6.0, 2.0, D).astype(np.float32)    # memory from ~400 steps to ~1
+    pc = rng.standard_normal(D).astype(np.float32)
+    h0 = rng.standard_normal((B, D)).astype(np.float32)
+    k = torch.from_numpy(kc).cuda()[None, None, :].expand(B, T, D).contiguous()
+    p = torch.from_numpy(pc).cuda()[None, None, :].expand(B, T, D).contiguous()
+    y = sr.mingru_forward(k=k, p=p, h0=dev(h0))
+    del k, p
+    ts = np.unique(np.concatenate([[1, 2, 143, 144, 145, 288, 289, 4096, 1 << 19, T - 1, T],
+                                   rng.integers(1, T + 1, 48)]))
+    got = host64(y[:, torch.from_numpy(ts - 1).to(y.device), :])
+    a = scalar.sigmoid(-kc.astype(np.float64))
+    b = scalar.sigmoid(kc.astype(np.float64)) * scalar.g(pc.astype(np.float64))
+    at = np.power(a[None, :], ts[:, None].astype(np.float64))          # [n_t, D]
+    carry = at[None] * h0.astype(np.float64)[:, None, :]
+    inp = (b * (1.0 - at) / (1.0 - a))[None]
+    ref = carry + inp
+    err = np.max(np.abs(got - ref) / (np.abs(carry) + inp))
+    say("closed-form error", err)
+    assert err < TOL_F32
+
+
+def test_two_streams_at_once():
+    """Two scans in flight together on two streams (separate workspaces):
+    their tiles interleave on the GPU; each result equals the same call made
+    alone, bit for bit, and the oracle."""
+    shapes = [(4, 8192, 512), (2, 20000, 256)]
+    ins = [_inputs(B, T, D, seed=82 + i, k_mean=-4.0, k_std=1.0) for i, (B, T, D) in enumerate(shapes)]
+    devs = [(dev(k), dev(p), dev(h0)) for k, p, h0 in ins]
+    alone = [sr.mingru_forward(k=k, p=p, h0=h0) for k, p, h0 in devs]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [None, None]
+    for rep in range(3):
+        for s in streams:
+            s.wait_stream(torch.cuda.current_stream())
+        for i, s in enumerate(streams):
+            with torch.cuda.stream(s):
+                k, p, h0 = devs[i]
+                outs[i] = sr.mingru_forward(k=k, p=p, h0=h0)
+        torch.cuda.synchronize()
+        for i in range(2):
+            assert torch.equal(outs[i], alone[i]), (rep, i)
+    for i, (k, p, h0) in enumerate(ins):
+        assert scan_err(host64(outs[i]), k, p, h0) < TOL_F32
