@@ -208,3 +208,27 @@ def test_mingru_backward_extreme_values():
     errs = _mingru_errors(k, p, h0, dh, dl, dk, dp, dh0)
     say("errors", errs)
     assert max(errs) < TOL, errs
+
+
+def test_mingru_backward_kp_halves_of_one_buffer():
+    """k and p as the two halves of one [B,T,2D] buffer (row stride 2D, as the
+    input projection writes them): the same gradients as from separate
+    contiguous tensors, bit for bit, and the oracle's."""
+    B, T, D = 2, 3000, 192
+    say("mingru bwd kp halves")
+    rng = np.random.default_rng(4100)
+    kp = rng.standard_normal((B, T, 2 * D)).astype(np.float32)
+    kp[..., :D] -= 2.0
+    h0 = rng.standard_normal((B, D)).astype(np.float32)
+    dh = rng.standard_normal((B, T, D)).astype(np.float32)
+    kpd = dev(kp)
+    k_view, p_view = kpd[..., :D], kpd[..., D:]
+    h = sr.mingru_forward(k=k_view, p=p_view, h0=dev(h0))
+    got = sr.mingru_scan_backward(k_view, p_view, h, dev(dh), h0=dev(h0))
+    sep = sr.mingru_scan_backward(k_view.contiguous(), p_view.contiguous(), h, dev(dh), h0=dev(h0))
+    for a, b in zip(got, sep):
+        assert torch.equal(a, b)
+    k, p = kp[..., :D], kp[..., D:]
+    errs = _mingru_errors(k, p, h0, dh, None, *got)
+    say("errors", errs)
+    assert max(errs) < TOL

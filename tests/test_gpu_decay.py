@@ -213,3 +213,27 @@ def test_full_size_b8_t65536_d1024_decayed_sampled():
         errs.append(_err(h[b, :, d][None, :, None], kc, pc, lam[d:d + 1], dt[b:b + 1], h0c, False))
     say("sampled errors", max(errs))
     assert max(errs) < TOL_F32
+
+
+def test_decayed_step_over_many_streams():
+    """1024 streams: the step's products split K across workgroups, and the
+    reduction kernel applies the decayed update."""
+    B, D_in, D_h = 1024, 512, 512
+    say("decayed step B=1024")
+    assert sr.raw_library().mingru_step_workspace_size(B, D_in, D_h, D_h) > 0
+    rng = np.random.default_rng(1204)
+    x_t = rng.standard_normal((B, D_in)).astype(np.float32)
+    W_in = (rng.standard_normal((D_in, 2 * D_h)) / D_in ** 0.5).astype(np.float32)
+    lam = (10.0 ** rng.uniform(-3, 0, D_h)).astype(np.float32)
+    dt = rng.exponential(1.0, B).astype(np.float32)
+    dt[::97] = 1e6
+    h0 = rng.standard_normal((B, D_h)).astype(np.float32)
+    for log1p in (False, True):
+        sat = torch.zeros(1, dtype=torch.int32, device="cuda")
+        _, h = sr.mingru_step_decayed(dev(x_t), dev(W_in), h_prev=dev(h0), decay_rate=dev(lam),
+                                      delta_t=dev(dt), log1p_delta=log1p, saturated=sat)
+        _, h_ref = decay.step(x_t, W_in, lam, dt, None, h0, log1p)
+        err = metrics.max_abs_rel(host64(h), h_ref)
+        say("log1p", log1p, "error", err)
+        assert err < TOL_F32
+        assert int(sat.item()) == int(decay.saturated(lam, dt, log1p))
