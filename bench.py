@@ -80,12 +80,12 @@ def time_launches(torch, fn, steps, warmup):
 
 def leg_scan(torch, sr, synth, steps, warmup, cpu_steps):
     import ctypes
-    cfg = synth.CONFIGS[3]
+    cfg = synth.CONFIGS[synth.SCAN]
     B, T, D = cfg["B"], cfg["T"], cfg["D"]
     log(f"[bench] scan B={B} T={T} D={D}: generating inputs")
-    kb = synth.device_normal(3, "k", (B, T, D), cfg["k_mean"], cfg["k_std"], torch.bfloat16)
-    pb = synth.device_normal(3, "p", (B, T, D), cfg["p_mean"], cfg["p_std"], torch.bfloat16)
-    h0 = synth.device_normal(3, "h0", (B, D))
+    kb = synth.device_normal(synth.SCAN, "k", (B, T, D), cfg["k_mean"], cfg["k_std"], torch.bfloat16)
+    pb = synth.device_normal(synth.SCAN, "p", (B, T, D), cfg["p_mean"], cfg["p_std"], torch.bfloat16)
+    h0 = synth.device_normal(synth.SCAN, "h0", (B, D))
     y = torch.empty((B, T, D), dtype=torch.float32, device="cuda")
     last = torch.empty((B, D), dtype=torch.float32, device="cuda")
     lib = sr.raw_library()
@@ -147,12 +147,12 @@ def leg_scan(torch, sr, synth, steps, warmup, cpu_steps):
 
 
 def leg_minmax(torch, sr, synth, steps, warmup):
-    cfg = synth.CONFIGS[5]
+    cfg = synth.CONFIGS[synth.MINMAX]
     B, T, D = cfg["B"], cfg["T"], cfg["D"]
     log(f"[bench] minmax B={B} T={T} D={D}")
-    r = synth.device_uniform(5, "r", (B, T, D), -1.0, 1.0)
-    s = synth.device_uniform(5, "s", (B, T, D), -1.5, 0.5)
-    x0 = synth.device_uniform(5, "x0", (B, D), -1.0, 1.0)
+    r = synth.device_uniform(synth.MINMAX, "r", (B, T, D), -1.0, 1.0)
+    s = synth.device_uniform(synth.MINMAX, "s", (B, T, D), -1.5, 0.5)
+    x0 = synth.device_uniform(synth.MINMAX, "x0", (B, D), -1.0, 1.0)
     out = torch.empty_like(r)
     last = torch.empty((B, D), device="cuda")
     ws = torch.empty(sr.raw_library().minmax_scan_workspace_size(B, T, D), dtype=torch.uint8,
@@ -173,11 +173,11 @@ def leg_minmax_step(torch, sr, synth, n_steps):
     """The MinMax neuron one token at a time at the MinMax workload's width
     (B=8, D=192), in place: eagerly and replayed from a HIP graph.  The final
     state is checked bit for bit against the scan over the same tokens."""
-    cfg = synth.CONFIGS[5]
+    cfg = synth.CONFIGS[synth.MINMAX]
     B, D = cfg["B"], cfg["D"]
-    r = synth.device_uniform(5, "r", (B, n_steps, D), -1.0, 1.0)
-    s = synth.device_uniform(5, "s", (B, n_steps, D), -1.5, 0.5)
-    x0 = synth.device_uniform(5, "x0", (B, D), -1.0, 1.0)
+    r = synth.device_uniform(synth.MINMAX, "r", (B, n_steps, D), -1.0, 1.0)
+    s = synth.device_uniform(synth.MINMAX, "s", (B, n_steps, D), -1.5, 0.5)
+    x0 = synth.device_uniform(synth.MINMAX, "x0", (B, D), -1.0, 1.0)
     rs = [r[:, t].contiguous() for t in range(n_steps)]
     ss = [s[:, t].contiguous() for t in range(n_steps)]
     x = torch.empty_like(x0)
@@ -221,12 +221,12 @@ def leg_minmax_step(torch, sr, synth, n_steps):
 def leg_scan_backward(torch, sr, synth, steps, warmup):
     """Backward of the headline scan: reads k, p (bf16), h, dh (fp32), writes
     dk, dp (fp32): 20 algorithmic bytes per element."""
-    cfg = synth.CONFIGS[3]
+    cfg = synth.CONFIGS[synth.SCAN]
     B, T, D = cfg["B"], cfg["T"], cfg["D"]
     log(f"[bench] scan backward B={B} T={T} D={D}")
-    kb = synth.device_normal(3, "k", (B, T, D), cfg["k_mean"], cfg["k_std"], torch.bfloat16)
-    pb = synth.device_normal(3, "p", (B, T, D), cfg["p_mean"], cfg["p_std"], torch.bfloat16)
-    h0 = synth.device_normal(3, "h0", (B, D))
+    kb = synth.device_normal(synth.SCAN, "k", (B, T, D), cfg["k_mean"], cfg["k_std"], torch.bfloat16)
+    pb = synth.device_normal(synth.SCAN, "p", (B, T, D), cfg["p_mean"], cfg["p_std"], torch.bfloat16)
+    h0 = synth.device_normal(synth.SCAN, "h0", (B, D))
     h = sr.mingru_forward(k=kb, p=pb, h0=h0)
     dh = torch.empty_like(h).normal_(0.0, 1.0)
     ws = torch.empty(sr.raw_library().mingru_scan_backward_workspace_size(B, T, D),
@@ -247,14 +247,14 @@ def leg_scan_decay(torch, sr, synth, steps, warmup):
     """The headline scan shape with time decay of the carried state: k, p
     (bf16) in, h (fp32) out as in the plain scan, plus one gap per (b, t) and
     one rate per channel: 8 + 4/D algorithmic bytes per element."""
-    cfg = synth.CONFIGS[3]
+    cfg = synth.CONFIGS[synth.SCAN]
     B, T, D = cfg["B"], cfg["T"], cfg["D"]
     log(f"[bench] decayed scan B={B} T={T} D={D}")
-    kb = synth.device_normal(3, "k", (B, T, D), cfg["k_mean"], cfg["k_std"], torch.bfloat16)
-    pb = synth.device_normal(3, "p", (B, T, D), cfg["p_mean"], cfg["p_std"], torch.bfloat16)
-    h0 = synth.device_normal(3, "h0", (B, D))
-    rate = torch.from_numpy(synth.decay_rates(3, D)).cuda()
-    gap = torch.from_numpy(synth.gaps(3, B, T)).cuda()
+    kb = synth.device_normal(synth.SCAN, "k", (B, T, D), cfg["k_mean"], cfg["k_std"], torch.bfloat16)
+    pb = synth.device_normal(synth.SCAN, "p", (B, T, D), cfg["p_mean"], cfg["p_std"], torch.bfloat16)
+    h0 = synth.device_normal(synth.SCAN, "h0", (B, D))
+    rate = torch.from_numpy(synth.decay_rates(synth.SCAN, D)).cuda()
+    gap = torch.from_numpy(synth.gaps(synth.SCAN, B, T)).cuda()
     sat = torch.zeros(1, dtype=torch.int32, device="cuda")
     y = torch.empty((B, T, D), dtype=torch.float32, device="cuda")
     ws = torch.empty(sr.raw_library().mingru_forward_workspace_size(B, T, 0, D, D, 0, 0),
@@ -279,12 +279,12 @@ def leg_scan_decay(torch, sr, synth, steps, warmup):
 def leg_minmax_backward(torch, sr, synth, steps, warmup):
     """Backward of the MinMax scan: reads r, s, x_out, dx, writes dr, ds
     (fp32): 24 algorithmic bytes per element."""
-    cfg = synth.CONFIGS[5]
+    cfg = synth.CONFIGS[synth.MINMAX]
     B, T, D = cfg["B"], cfg["T"], cfg["D"]
     log(f"[bench] minmax backward B={B} T={T} D={D}")
-    r = synth.device_uniform(5, "r", (B, T, D), -1.0, 1.0)
-    s = synth.device_uniform(5, "s", (B, T, D), -1.5, 0.5)
-    x0 = synth.device_uniform(5, "x0", (B, D), -1.0, 1.0)
+    r = synth.device_uniform(synth.MINMAX, "r", (B, T, D), -1.0, 1.0)
+    s = synth.device_uniform(synth.MINMAX, "s", (B, T, D), -1.5, 0.5)
+    x0 = synth.device_uniform(synth.MINMAX, "x0", (B, D), -1.0, 1.0)
     x_out = sr.minmax_scan(r, s, x0)
     dx = torch.empty_like(r).normal_(0.0, 1.0)
     ws = torch.empty(sr.raw_library().minmax_scan_backward_workspace_size(B, T, D),
@@ -299,12 +299,12 @@ def leg_minmax_backward(torch, sr, synth, steps, warmup):
 
 
 def leg_decode(torch, sr, synth, n_steps):
-    cfg = synth.CONFIGS[4]
+    cfg = synth.CONFIGS[synth.STEP]
     B, D, Tp = cfg["B"], cfg["D"], cfg["T_prefill"]
     log(f"[bench] decode: prefill B={B} T={Tp} D={D}, then {n_steps} steps")
-    W_in = synth.device_normal(4, "W_in", (D, 2 * D), 0.0, cfg["w_std"])
-    W_out = synth.device_normal(4, "W_out", (D, D), 0.0, cfg["w_std"])
-    x = synth.device_normal(4, "x", (B, Tp + n_steps, D))
+    W_in = synth.device_normal(synth.STEP, "W_in", (D, 2 * D), 0.0, cfg["w_std"])
+    W_out = synth.device_normal(synth.STEP, "W_out", (D, D), 0.0, cfg["w_std"])
+    x = synth.device_normal(synth.STEP, "x", (B, Tp + n_steps, D))
     torch.cuda.synchronize()
     # Prefill (parallel forward over 512 steps), timed on its own.
     y, h = sr.mingru_forward(x[:, :Tp], W_in, W_out=W_out, return_last=True)
@@ -336,12 +336,12 @@ def leg_decode(torch, sr, synth, n_steps):
                 step_frac_fp32_mfma=step_flops * n_steps / t_steps / 1e12 / FP32_MFMA_PEAK_TFLOPS)
 
 
-def leg_layer(torch, sr, synth, cfg_id, steps):
-    cfg = synth.CONFIGS[cfg_id]
+def leg_layer(torch, sr, synth, workload, steps):
+    cfg = synth.CONFIGS[workload]
     B, T, D = cfg["B"], cfg["T"], cfg["D"]
-    x = synth.device_normal(cfg_id, "x", (B, T, D))
-    W_in = synth.device_normal(cfg_id, "W_in", (D, 2 * D), 0.0, cfg["w_std"])
-    W_out = synth.device_normal(cfg_id, "W_out", (D, D), 0.0, cfg["w_std"])
+    x = synth.device_normal(workload, "x", (B, T, D))
+    W_in = synth.device_normal(workload, "W_in", (D, 2 * D), 0.0, cfg["w_std"])
+    W_out = synth.device_normal(workload, "W_out", (D, D), 0.0, cfg["w_std"])
     wall, mean_ms, _ = time_launches(torch, lambda: sr.mingru_forward(x, W_in, W_out=W_out),
                                      steps, 3)
     res = dict(B=B, T=T, D=D, forward_ms=wall / steps * 1e3, forward_launch_ms=mean_ms,
@@ -409,7 +409,7 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
         sys.exit(2)
 
@@ -438,9 +438,9 @@ def main():
     if "scan_decay" in legs:
         extra["decayed_b8_t65536_d1024"] = leg_scan_decay(torch, sr, synth, args.steps, args.warmup)
     if "layer_d512" in legs:
-        extra["layer_b2_t1024_d512"] = leg_layer(torch, sr, synth, 2, 10)
+        extra["layer_b2_t1024_d512"] = leg_layer(torch, sr, synth, synth.LAYER, 10)
     if "layer_d16" in legs:
-        extra["layer_b2_t64_d16"] = leg_layer(torch, sr, synth, 1, 10)
+        extra["layer_b2_t64_d16"] = leg_layer(torch, sr, synth, synth.LAYER_TINY, 10)
     if "decode" in legs:
         extra["step_b256_d2048"] = leg_decode(torch, sr, synth, args.decode_steps)
     if "minmax_step" in legs:

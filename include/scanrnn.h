@@ -59,7 +59,7 @@ extern "C" {
 typedef enum {
   SR_OK = 0,
   SR_ERR_INVALID_ARGUMENT = 1,   /* null pointer, negative size, bad stride     */
-  SR_ERR_UNSUPPORTED = 2,        /* valid request this build does not handle    */
+  SR_ERR_UNSUPPORTED = 2,        /* valid request the library does not handle   */
   SR_ERR_WORKSPACE_TOO_SMALL = 3,
   SR_ERR_HIP = 4,                /* a HIP runtime call failed                   */
   SR_ERR_LOOKBACK_TIMEOUT = 5    /* reported by scanrnn_workspace_status only   */

@@ -8,6 +8,11 @@ compute code.
 
 from .inputs import (  # noqa: F401
     CONFIGS,
+    LAYER,
+    LAYER_TINY,
+    MINMAX,
+    SCAN,
+    STEP,
     TENSOR_IDS,
     T_BLOCK,
     bf16_round,

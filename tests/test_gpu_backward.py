@@ -83,11 +83,11 @@ def test_mingru_backward_f32(B, T, D, with_h0, with_last):
 def test_mingru_backward_bf16_long_memory_reduced():
     B, T, D = 2, 4096, 1024
     say("mingru bwd bf16")
-    cfg = synth.CONFIGS[3]
-    k32 = synth.normal_bt(3, "k", B, T, D, cfg["k_mean"], cfg["k_std"])
-    p32 = synth.normal_bt(3, "p", B, T, D, cfg["p_mean"], cfg["p_std"])
+    cfg = synth.CONFIGS[synth.SCAN]
+    k32 = synth.normal_bt(synth.SCAN, "k", B, T, D, cfg["k_mean"], cfg["k_std"])
+    p32 = synth.normal_bt(synth.SCAN, "p", B, T, D, cfg["p_mean"], cfg["p_std"])
     kb, pb = synth.bf16_round(k32).cuda(), synth.bf16_round(p32).cuda()
-    h0 = synth.normal_vec(3, "h0", B, D)
+    h0 = synth.normal_vec(synth.SCAN, "h0", B, D)
     rng = np.random.default_rng(1101)
     dh = rng.standard_normal((B, T, D)).astype(np.float32)
     dl = rng.standard_normal((B, D)).astype(np.float32)
@@ -162,12 +162,12 @@ def test_minmax_backward_hold_and_reset():
 
 
 def test_full_size_b8_t65536_d1024_backward_sampled():
-    cfg = synth.CONFIGS[3]
+    cfg = synth.CONFIGS[synth.SCAN]
     B, T, D = cfg["B"], cfg["T"], cfg["D"]
     say("full size B=8 T=65536 D=1024 backward")
-    kb = synth.device_normal(3, "k", (B, T, D), cfg["k_mean"], cfg["k_std"], torch.bfloat16)
-    pb = synth.device_normal(3, "p", (B, T, D), cfg["p_mean"], cfg["p_std"], torch.bfloat16)
-    h0 = synth.device_normal(3, "h0", (B, D))
+    kb = synth.device_normal(synth.SCAN, "k", (B, T, D), cfg["k_mean"], cfg["k_std"], torch.bfloat16)
+    pb = synth.device_normal(synth.SCAN, "p", (B, T, D), cfg["p_mean"], cfg["p_std"], torch.bfloat16)
+    h0 = synth.device_normal(synth.SCAN, "h0", (B, D))
     g = torch.Generator(device="cuda")
     g.manual_seed(1130)
     dh = torch.empty((B, T, D), device="cuda").normal_(0.0, 1.0, generator=g)

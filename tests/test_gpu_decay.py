@@ -59,14 +59,14 @@ def test_decayed_scan_f32(B, T, D, with_h0, log1p, huge):
 
 
 def test_decayed_scan_bf16_long_memory_reduced():
-    cfg = synth.CONFIGS[3]
+    cfg = synth.CONFIGS[synth.SCAN]
     B, T, D = 2, 4096, 1024
     say("decay bf16 long-memory B=2 T=4096 D=1024")
-    kb = synth.bf16_round(synth.normal_bt(3, "k", B, T, D, cfg["k_mean"], cfg["k_std"])).cuda()
-    pb = synth.bf16_round(synth.normal_bt(3, "p", B, T, D, cfg["p_mean"], cfg["p_std"])).cuda()
-    h0 = synth.normal_vec(3, "h0", B, D)
-    lam = synth.decay_rates(3, D)
-    dt = synth.gaps(3, B, T)
+    kb = synth.bf16_round(synth.normal_bt(synth.SCAN, "k", B, T, D, cfg["k_mean"], cfg["k_std"])).cuda()
+    pb = synth.bf16_round(synth.normal_bt(synth.SCAN, "p", B, T, D, cfg["p_mean"], cfg["p_std"])).cuda()
+    h0 = synth.normal_vec(synth.SCAN, "h0", B, D)
+    lam = synth.decay_rates(synth.SCAN, D)
+    dt = synth.gaps(synth.SCAN, B, T)
     sat = torch.zeros(1, dtype=torch.int32, device="cuda")
     h = sr.mingru_forward_decayed(k=kb, p=pb, h0=dev(h0), decay_rate=dev(lam), delta_t=dev(dt),
                                   saturated=sat)
@@ -187,14 +187,14 @@ def test_decayed_step_loop_matches_oracle():
 
 
 def test_full_size_b8_t65536_d1024_decayed_sampled():
-    cfg = synth.CONFIGS[3]
+    cfg = synth.CONFIGS[synth.SCAN]
     B, T, D = cfg["B"], cfg["T"], cfg["D"]
     say("decay full size B=8 T=65536 D=1024")
-    kb = synth.device_normal(3, "k", (B, T, D), cfg["k_mean"], cfg["k_std"], torch.bfloat16)
-    pb = synth.device_normal(3, "p", (B, T, D), cfg["p_mean"], cfg["p_std"], torch.bfloat16)
-    h0 = synth.device_normal(3, "h0", (B, D))
-    lam = synth.decay_rates(3, D)
-    dt = synth.gaps(3, B, T)
+    kb = synth.device_normal(synth.SCAN, "k", (B, T, D), cfg["k_mean"], cfg["k_std"], torch.bfloat16)
+    pb = synth.device_normal(synth.SCAN, "p", (B, T, D), cfg["p_mean"], cfg["p_std"], torch.bfloat16)
+    h0 = synth.device_normal(synth.SCAN, "h0", (B, D))
+    lam = synth.decay_rates(synth.SCAN, D)
+    dt = synth.gaps(synth.SCAN, B, T)
     sat = torch.zeros(1, dtype=torch.int32, device="cuda")
     ws = torch.empty(sr.raw_library().mingru_forward_workspace_size(B, T, 0, D, D, 0, 0),
                      dtype=torch.uint8, device="cuda")

@@ -15,12 +15,12 @@ pytestmark = pytest.mark.gpu
 sr = pytest.importorskip("scan_linear_rnn_amd")
 
 
-def _layer_inputs(cfg_id):
-    cfg = synth.CONFIGS[cfg_id]
+def _layer_inputs(workload):
+    cfg = synth.CONFIGS[workload]
     B, T, D = cfg["B"], cfg["T"], cfg["D"]
-    x = synth.normal_bt(cfg_id, "x", B, T, D)
-    W_in = synth.normal_mat(cfg_id, "W_in", D, 2 * D, cfg["w_std"])
-    W_out = synth.normal_mat(cfg_id, "W_out", D, D, cfg["w_std"])
+    x = synth.normal_bt(workload, "x", B, T, D)
+    W_in = synth.normal_mat(workload, "W_in", D, 2 * D, cfg["w_std"])
+    W_out = synth.normal_mat(workload, "W_out", D, D, cfg["w_std"])
     return x, W_in, W_out
 
 
@@ -40,10 +40,10 @@ def _check_layer(x, W_in, W_out, h0=None, tol=TOL_F32):
     return y
 
 
-@pytest.mark.parametrize("cfg_id", [1, 2])
-def test_layer_workloads_match_oracle(cfg_id):
-    say(f"layer workload {synth.CONFIGS[cfg_id]['name']}")
-    x, W_in, W_out = _layer_inputs(cfg_id)
+@pytest.mark.parametrize("workload", [synth.LAYER_TINY, synth.LAYER])
+def test_layer_workloads_match_oracle(workload):
+    say(f"layer workload {workload}")
+    x, W_in, W_out = _layer_inputs(workload)
     y = _check_layer(x, W_in, W_out)
     assert tuple(y.shape) == x.shape  # output has the input's shape
 
@@ -69,7 +69,7 @@ def test_step_loop_matches_oracle_and_parallel_mode():
     checked against the oracle's step, and the final state against the
     parallel forward (the pages' parallel-vs-sequential comparison)."""
     say("step loop B=2 T=1024 D=512")
-    x, W_in, W_out = _layer_inputs(2)
+    x, W_in, W_out = _layer_inputs(synth.LAYER)
     B, T, D = x.shape
     xd, Wi, Wo = dev(x), dev(W_in), dev(W_out)
     y_par, h_par = sr.mingru_forward(xd, Wi, W_out=Wo, return_last=True)
@@ -130,12 +130,12 @@ def test_decode_b256_d2048():
     parallel forward over the concatenated 4608-step sequence; two seeded
     rows are also checked against the fp64 oracle after steps 1, 2, 8 and at
     the end (the prefill's carry is still visible in the first steps)."""
-    cfg = synth.CONFIGS[4]
+    cfg = synth.CONFIGS[synth.STEP]
     B, D, Tp, S = cfg["B"], cfg["D"], cfg["T_prefill"], cfg["steps"]
     say("decode B=256 D=2048")
-    W_in = synth.device_normal(4, "W_in", (D, 2 * D), 0.0, cfg["w_std"])
-    W_out = synth.device_normal(4, "W_out", (D, D), 0.0, cfg["w_std"])
-    x = synth.device_normal(4, "x", (B, Tp + S, D))
+    W_in = synth.device_normal(synth.STEP, "W_in", (D, 2 * D), 0.0, cfg["w_std"])
+    W_out = synth.device_normal(synth.STEP, "W_out", (D, D), 0.0, cfg["w_std"])
+    x = synth.device_normal(synth.STEP, "x", (B, Tp + S, D))
     _, h = sr.mingru_forward(x[:, :Tp], W_in, W_out=W_out, return_last=True)
     rows = [3, 201]
     snaps = {}

@@ -36,13 +36,13 @@ def test_minmax_bitwise(B, T, D):
 
 
 def test_minmax_full_size_b8_t32768_d192_bitwise():
-    cfg = synth.CONFIGS[5]
+    cfg = synth.CONFIGS[synth.MINMAX]
     B, T, D = cfg["B"], cfg["T"], cfg["D"]
     say("minmax full size B=8 T=32768 D=192")
-    r = synth.uniform_bt(5, "r", B, T, D, -1.0, 1.0)
-    s = synth.uniform_bt(5, "s", B, T, D, -1.0, 1.0) - np.float32(0.5)
+    r = synth.uniform_bt(synth.MINMAX, "r", B, T, D, -1.0, 1.0)
+    s = synth.uniform_bt(synth.MINMAX, "s", B, T, D, -1.0, 1.0) - np.float32(0.5)
     s[s == 0] = 0.0
-    x0 = synth.uniform_vec(5, "x0", B, D, -1.0, 1.0)
+    x0 = synth.uniform_vec(synth.MINMAX, "x0", B, D, -1.0, 1.0)
     out, last = sr.minmax_scan(dev(r), dev(s), dev(x0), return_last=True)
     ref, ref_last = minmax.scan(r, s, x0)
     assert metrics.bits_equal(out.cpu().numpy(), ref)

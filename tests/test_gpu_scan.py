@@ -44,10 +44,10 @@ def test_scan_f32_matches_oracle(B, T, D, with_h0):
 def test_scan_bf16_long_memory_statistics():
     B, T, D = 2, 4096, 1024
     say(f"scan bf16 long-memory B={B} T={T} D={D}")
-    cfg = synth.CONFIGS[3]
-    k32 = synth.normal_bt(3, "k", B, T, D, cfg["k_mean"], cfg["k_std"])
-    p32 = synth.normal_bt(3, "p", B, T, D, cfg["p_mean"], cfg["p_std"])
-    h0 = synth.normal_vec(3, "h0", B, D)
+    cfg = synth.CONFIGS[synth.SCAN]
+    k32 = synth.normal_bt(synth.SCAN, "k", B, T, D, cfg["k_mean"], cfg["k_std"])
+    p32 = synth.normal_bt(synth.SCAN, "p", B, T, D, cfg["p_mean"], cfg["p_std"])
+    h0 = synth.normal_vec(synth.SCAN, "h0", B, D)
     kb, pb = synth.bf16_round(k32), synth.bf16_round(p32)
     y = sr.mingru_forward(k=kb.cuda(), p=pb.cuda(), h0=dev(h0))
     # The oracle reads the same bf16 values.
@@ -132,12 +132,12 @@ def test_full_size_b8_t65536_d1024_sampled_channels():
     launched exactly as the benchmark launches it; 24 sampled channels are
     checked over all 65536 steps against the oracle, and every output must be
     finite."""
-    cfg = synth.CONFIGS[3]
+    cfg = synth.CONFIGS[synth.SCAN]
     B, T, D = cfg["B"], cfg["T"], cfg["D"]
     say("full size B=8 T=65536 D=1024 sampled")
-    kb = synth.device_normal(3, "k", (B, T, D), cfg["k_mean"], cfg["k_std"], torch.bfloat16)
-    pb = synth.device_normal(3, "p", (B, T, D), cfg["p_mean"], cfg["p_std"], torch.bfloat16)
-    h0 = synth.device_normal(3, "h0", (B, D))
+    kb = synth.device_normal(synth.SCAN, "k", (B, T, D), cfg["k_mean"], cfg["k_std"], torch.bfloat16)
+    pb = synth.device_normal(synth.SCAN, "p", (B, T, D), cfg["p_mean"], cfg["p_std"], torch.bfloat16)
+    h0 = synth.device_normal(synth.SCAN, "h0", (B, D))
     ws = torch.empty(sr.raw_library().mingru_forward_workspace_size(B, T, 0, D, D, 0, 0),
                      dtype=torch.uint8, device="cuda")
     y, last = sr.mingru_forward(k=kb, p=pb, h0=h0, return_last=True, workspace=ws)
