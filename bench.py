@@ -46,16 +46,22 @@ METRIC = ("scan elements/s (B·T·D) + achieved HBM GB/s vs peak, "
 HBM_PEAK_GBPS = 8000.0
 FP32_MFMA_PEAK_TFLOPS = 157.3
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_b8_t65536_d1024_bf16_traffic.json")
-SCAN_SOURCE = os.path.join(ROOT, "scan_linear_rnn_amd", "csrc", "scan.hip")
+# The scan kernel's sources: the kernel and the engine it instantiates.
+SCAN_SOURCES = [os.path.join(ROOT, "scan_linear_rnn_amd", "csrc", f)
+                for f in ("scan.hip", "scan_engine.hpp")]
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def source_hash(path=SCAN_SOURCE) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_hash(paths=SCAN_SOURCES) -> str:
+    """First 16 hex digits of the SHA-256 of the scan kernel's sources, in order."""
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def time_launches(torch, fn, steps, warmup):

@@ -137,7 +137,7 @@ void fused_proj_scan_kernel(const FusedParams F) {
   // 3. Wave rows along T, then the look-back across tiles.
   if (kl == 0) s_pre[wm][c] = run;
   __syncthreads();
-  resolve_tile<MinGRUOp, kTileT / 64, kTileD, 2 * kTileT>(P, tl, s_pre, s_win, s_hin);
+  resolve_tile<MinGRUOp, kTileT / 64, kTileD, 2 * kTileT, 2>(P, tl, s_pre, s_win, s_hin);
 
   // 4. Replay and store.
   const float h_wave = MinGRUOp::apply(s_pre[wm][c], s_hin[c]);

@@ -186,41 +186,76 @@ struct ScanParams {
 constexpr float kDecayClamp = 1.0e4f;
 constexpr float kNegLog2e = -1.4426950408889634f;
 
-// Look-back along T for one channel, one tile at a time: used when the
-// window fetched in one round trip holds no usable end state.  Returns the
-// state entering tile `tchunk` of batch row b, channel d.
-template <class Op>
+// Look-back along T for one channel, used when the window fetched in one
+// round trip holds no usable end state.  Returns the state entering tile
+// `tchunk` of batch row b, channel d.  Walks back kB words per
+// round trip to the nearest published end state (position -1 stands for the
+// initial state; an unwritten word is polled, bounded), then applies the maps
+// of the tiles after it one by one in order, again kB loads per
+// round trip.  One apply per tile, in order, from an end state: the same fma
+// sequence as the tiles' own end states, whatever the depth reached.
+constexpr int kSerialBatch = 4;  // default words per round trip (register cost: 2 VGPRs each)
+
+template <class Op, int kB>
 __device__ float lookback_serial(const ScanParams& P, int64_t tchunk, int64_t b, int64_t d) {
   const size_t plane = size_t(P.B) * size_t(P.D);
   const uint64_t* col = P.state + size_t(b) * size_t(P.D) + size_t(d);
-  float h = (P.init != nullptr) ? P.init[size_t(b) * P.D + d] : 0.0f;
-  // Backward: find the nearest earlier tile whose end state is published.
-  int64_t i = tchunk - 1;
+  const float h_init = (P.init != nullptr) ? P.init[size_t(b) * P.D + d] : 0.0f;
+  float h = h_init;
+  // Backward.  tchunk >= 1, and the batch that reaches position -1 holds the
+  // initial state there, so the loop ends with an end state found.
+  int64_t top = tchunk - 1;
+  int64_t found = -1;
   uint32_t spins = 0;
-  while (i >= 0) {
-    const uint64_t w = load_word(col + size_t(i) * plane);
-    const uint32_t hi = uint32_t(w >> 32);
-    if (hi == kTagState) {
-      h = __uint_as_float(uint32_t(w));
-      break;
+  for (;;) {
+    uint64_t w[kB];
+#pragma unroll
+    for (int q = 0; q < kB; ++q)
+      w[q] = top - q >= 0 ? load_word(col + size_t(top - q) * plane) : pack_state(h_init);
+    // First position (nearest tile) that is not a published map.
+    int stop = kB;
+#pragma unroll
+    for (int q = kB - 1; q >= 0; --q) {
+      const uint32_t hi = uint32_t(w[q] >> 32);
+      if (hi == kTagState || hi == kTagEmpty) stop = q;
     }
-    if (hi != kTagEmpty) {
-      --i;  // a published map: keep walking (tile 0 publishes only its state)
+    if (stop == kB) {  // kB maps: the next batch
+      top -= kB;
       continue;
     }
+    uint64_t ws = 0;
+#pragma unroll
+    for (int q = 0; q < kB; ++q)
+      if (q == stop) ws = w[q];
+    if (uint32_t(ws >> 32) == kTagState) {
+      h = __uint_as_float(uint32_t(ws));
+      found = top - stop;
+      break;
+    }
+    // Tile top - stop has not published yet: poll its word.
     if (++spins > kSpinLimit) {
       __hip_atomic_store(P.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       return __uint_as_float(kCanonNaN);
     }
     __builtin_amdgcn_s_sleep(8);  // ~512 cycles between polls of an unwritten word
+    top -= stop;
   }
-  // Forward: apply the maps of tiles i+1 .. tchunk-1 in order.
-  for (int64_t m = i + 1; m < tchunk; ++m) {
-    const uint64_t wm = load_word(col + size_t(m) * plane);
-    if (uint32_t(wm >> 32) == kTagState)
-      h = __uint_as_float(uint32_t(wm));  // tile m finished meanwhile: same value
-    else
-      h = Op::apply(unpack_map(wm), h);
+  // Forward: the maps of tiles found+1 .. tchunk-1, in order.  Every one was
+  // seen published above; one that has meanwhile become an end state holds
+  // the same value the apply would give.
+  for (int64_t m0 = found + 1; m0 < tchunk; m0 += kB) {
+    uint64_t w[kB];
+#pragma unroll
+    for (int q = 0; q < kB; ++q) w[q] = m0 + q < tchunk ? load_word(col + size_t(m0 + q) * plane) : 0;
+#pragma unroll
+    for (int q = 0; q < kB; ++q) {
+      if (m0 + q < tchunk) {
+        if (uint32_t(w[q] >> 32) == kTagState)
+          h = __uint_as_float(uint32_t(w[q]));
+        else
+          h = Op::apply(unpack_map(w[q]), h);
+      }
+    }
   }
   return h;
 }
@@ -255,7 +290,7 @@ __device__ __forceinline__ Tile decode_ticket(const ScanParams& P, uint32_t tick
 // barrier, after which s_pre and s_hin are ready for phase 3.  W is the
 // number of segments along T (waves of the scan kernel), NT the number of
 // threads in the workgroup (a multiple of Dc, at least Dc).
-template <class Op, int W, int Dc, int NT = 64 * W>
+template <class Op, int W, int Dc, int NT = 64 * W, int SB = kSerialBatch>
 __device__ __forceinline__ void resolve_tile(const ScanParams& P, const Tile& tl,
                                              Pair (&s_pre)[W][Dc],
                                              uint64_t (&s_win)[kWindowTiles][Dc],
@@ -316,7 +351,7 @@ __device__ __forceinline__ void resolve_tile(const ScanParams& P, const Tile& tl
       for (int q = found - 1; q >= 0; --q) h = Op::apply(unpack_map(s_win[q][tid]), h);
       hin = h;
     } else {
-      hin = lookback_serial<Op>(P, tl.tchunk, tl.b, dc);
+      hin = lookback_serial<Op, SB>(P, tl.tchunk, tl.b, dc);
     }
   }
   if (chan_on) {
