@@ -202,6 +202,7 @@ sr_status launch_fused_forward(const FusedRequest& rq) {
   P.counter = reinterpret_cast<uint32_t*>(ws);
   P.status = reinterpret_cast<uint32_t*>(ws) + 1;
   P.state = reinterpret_cast<uint64_t*>(ws + eng::kHeaderBytes);
+  P.window = eng::kWindowTiles;
   P.rate = rq.decay_rate;
   P.gap = rq.delta_t;
   P.log1p_gap = rq.log1p_delta;

@@ -291,6 +291,7 @@ sr_status launch_scan_backward(const BackwardRequest& rq) {
   P.counter = reinterpret_cast<uint32_t*>(ws);
   P.status = reinterpret_cast<uint32_t*>(ws) + 1;
   P.state = reinterpret_cast<uint64_t*>(ws + kHeaderBytes);
+  P.window = kWindowTiles;
   Q.in0 = rq.in0;
   Q.in1 = rq.in1;
   Q.ld_in = rq.ld_in;

@@ -18,7 +18,7 @@ constexpr size_t kHeaderBytes = 256;
 constexpr int kWaves = 12;           // waves per workgroup
 constexpr int kElemsPerLane = 24;    // N * V: maps each lane keeps in registers
 constexpr int kWavesPerSimd = 6;     // register budget: waves resident per SIMD
-constexpr int kWindowTiles = 4;      // preceding tiles whose look-back words one round trip fetches
+constexpr int kWindowTiles = 4;      // most preceding tiles whose look-back words one round trip fetches
 
 struct Pair {
   float u, v;
@@ -169,6 +169,7 @@ struct ScanParams {
   uint32_t* counter;  // header word 0: ticket counter
   uint32_t* status;   // header word 1: timeout flag
   uint64_t* state;    // [n_tchunks][B][D] look-back words
+  int window;         // look-back words fetched per tile in the first round trip, 1..kWindowTiles
   // Time decay of the carried state (minGRU only; unused when rate is null).
   const float* rate;     // [D] per-channel decay rate
   const float* gap;      // [B,T] gap preceding each token
@@ -282,11 +283,12 @@ __device__ __forceinline__ Tile decode_ticket(const ScanParams& P, uint32_t tick
 // follows phase 1 (which left each wave's map of each channel in s_pre).
 // One thread per channel turns s_pre[w] into wave w's exclusive prefix and
 // forms the tile's map, which is published; all threads then fetch the
-// look-back words of the kWindowTiles preceding tiles in one round trip.
+// look-back words of the P.window preceding tiles in one round trip.
 // The nearest published end state, followed by the maps of the tiles after
 // it applied one by one in order, gives the state entering the tile, written
 // to s_hin; only if the window holds no usable end state does a thread walk
-// back tile by tile.  The tile's end state is published last.  Ends with a
+// back further (lookback_serial, SB words per round trip).  The tile's end
+// state is published last.  Ends with a
 // barrier, after which s_pre and s_hin are ready for phase 3.  W is the
 // number of segments along T (waves of the scan kernel), NT the number of
 // threads in the workgroup (a multiple of Dc, at least Dc).
@@ -295,7 +297,7 @@ __device__ __forceinline__ void resolve_tile(const ScanParams& P, const Tile& tl
                                              Pair (&s_pre)[W][Dc],
                                              uint64_t (&s_win)[kWindowTiles][Dc],
                                              float (&s_hin)[Dc]) {
-  constexpr int kWin = kWindowTiles;
+  const int kWin = P.window;  // in [1, kWindowTiles], uniform over the launch
   const int tid = threadIdx.x;
   const bool chan_thread = tid < Dc;
   const int64_t dc = tl.d0 + tid;
