@@ -208,23 +208,43 @@ constexpr int kNarrowMaxM = 512;
 constexpr int kNarrowKG = 8;  // waves (K groups) per workgroup
 constexpr int kNarrowSK = 16; // K per pipeline stage
 
-template <int TM>
+template <int TM, bool FULL>
 struct Narrow {
   static constexpr int kRI = TM / 32;                       // row blocks per wave
   static constexpr int kThreads = 64 * kNarrowKG;
   static constexpr int kAPer = TM * kNarrowSK / 64;         // A floats per thread
   static constexpr int kBPer = kNarrowSK * kNarrowCols / 64;  // B floats per thread (16)
-  // A is staged row-major ([row][k], rows of kNarrowSK + 4 floats: 16-byte
-  // aligned, and eight consecutive rows start in distinct groups of four
-  // banks, so 16-byte reads of eight lanes do not conflict); B as [k][col].
-  static constexpr int kLdA = kNarrowSK + 4, kLdB = kNarrowCols + PAD, kLdR = kNarrowCols + PAD;
+  // A is staged row-major, [row][k], B as [k][col].  Full tiles are loaded
+  // straight from global memory into LDS (16 bytes per lane, the lanes of an
+  // instruction filling 1 KiB in lane order), so their rows are unpadded and
+  // the four 16-byte chunks of an A row are stored in the order chunk ^
+  // ((row >> 1) & 3): the 16-byte reads of eight consecutive rows then hit
+  // distinct banks.  The register-staged path pads rows instead (A rows of
+  // 20 floats: 16-byte aligned, eight consecutive rows in distinct banks).
+  static constexpr int kLdA = FULL ? kNarrowSK : kNarrowSK + 4;
+  static constexpr int kLdB = FULL ? kNarrowCols : kNarrowCols + PAD;
+  static constexpr int kLdR = kNarrowCols + PAD;
   static constexpr int kStageFloats = TM * kLdA + kNarrowSK * kLdB;
-  static constexpr int kSmemFloats = kNarrowKG * 2 * kStageFloats;
+  static constexpr int kStagingFloats = kNarrowKG * 2 * kStageFloats;
+  static constexpr int kRedFloats = kNarrowKG * TM * kLdR;  // the waves' sums, over the staging
+  static constexpr int kSmemFloats = kStagingFloats > kRedFloats ? kStagingFloats : kRedFloats;
   static_assert(TM == 32 || TM == 64, "tile rows");
   static_assert(kAPer % 4 == 0 && kBPer % 4 == 0, "16-byte staging");
-  static_assert(kNarrowKG * TM * kLdR <= kSmemFloats, "the waves' sums reuse the staging LDS");
+  static_assert(!FULL || (kLdA == 16 && kLdB == 64), "direct loads fill unpadded 1 KiB blocks");
   static_assert(kSmemFloats * 4 <= 160 * 1024, "LDS of one CU");
 };
+
+// Copies 16 bytes per lane from global memory straight into LDS
+// (global_load_lds_dwordx4): lane l's bytes land at lds_block + 16 l, for the
+// wave-uniform lds_block.  Completion is tracked by vmcnt.
+__device__ __forceinline__ void load_lds16(const float* src, float* lds_block) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_block, 16, 0, 0);
+}
+
+// Waits until this wave's direct loads have landed in LDS (vmcnt) and its
+// LDS reads have returned (lgkmcnt), so that the next stage may read the one
+// buffer and overwrite the other.
+__device__ __forceinline__ void wait_stage() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory"); }
 
 __device__ __forceinline__ void put4(float* r, int q, float4 v) {
   r[4 * q] = v.x; r[4 * q + 1] = v.y; r[4 * q + 2] = v.z; r[4 * q + 3] = v.w;
@@ -247,7 +267,7 @@ __device__ __forceinline__ bool narrow_col_ok(const GemmParams& P, int64_t n0, i
 
 template <int MODE, int TM, bool FULL>
 __global__ __launch_bounds__(64 * kNarrowKG) void narrow_kernel(const GemmParams P) {
-  using G = Narrow<TM>;
+  using G = Narrow<TM, FULL>;
   constexpr int SK = kNarrowSK, KG = kNarrowKG, RI = G::kRI;
   __shared__ __align__(16) float smem[G::kSmemFloats];
   const int tid = threadIdx.x;
@@ -265,14 +285,16 @@ __global__ __launch_bounds__(64 * kNarrowKG) void narrow_kernel(const GemmParams
   const int64_t per = (n_kt + KG - 1) / KG;
   const int64_t kt0 = g * per;
   const int64_t kt1 = kt0 + per < n_kt ? kt0 + per : n_kt;
-  const int iters = int(per);  // the same for every wave (shared barriers)
+  const int iters = int(per);  // the same for every wave
 
-  float* As = smem + g * 2 * G::kStageFloats;  // [2][TM][kLdA]
-  float* Bs = As + TM * G::kLdA;               // [2][SK][kLdB], stage stride kStageFloats
-  auto a_vec4 = [&](int buf, int row, int k) -> float4& {
-    return *reinterpret_cast<float4*>(As + buf * G::kStageFloats + row * G::kLdA + k);
+  // This wave's two stages, kStageFloats apart: A [TM][kLdA], then B [SK][kLdB].
+  float* const stages = smem + g * 2 * G::kStageFloats;
+  auto stage_at = [&](int buf) { return stages + buf * G::kStageFloats; };
+  // Offset of A's 4-float chunk (row, k .. k + 3) in a stage (swizzled when full).
+  auto a_off = [](int row, int k) {
+    return row * G::kLdA + (FULL ? (((k >> 2) ^ ((row >> 1) & 3)) << 2) : k);
   };
-  auto b_at = [&](int buf, int k, int c) -> float& { return Bs[buf * G::kStageFloats + k * G::kLdB + c]; };
+  auto b_off = [](int k, int c) { return TM * G::kLdA + k * G::kLdB + c; };
 
   // Staging, in float4 chunks.  A chunk q of a lane: row q * 16 + lane / 4,
   // k (lane % 4) * 4, so one load instruction covers 16 whole row segments
@@ -288,17 +310,24 @@ __global__ __launch_bounds__(64 * kNarrowKG) void narrow_kernel(const GemmParams
   const bool b_cols_ok = narrow_col_ok<MODE>(P, n0, b_c + 3);  // the chunk's last column
   const int64_t gc = narrow_col<MODE>(P, n0, b_c);
   float ra[4 * kAQ], rb[4 * kBQ];  // plain floats: kept in registers
-  const float* a_ptr = P.A + (m0 + a_r) * P.lda + kt0 * SK + a_k;
+  // Full tiles: the lane's A chunk goes to slot lane % 4 of its row, which
+  // holds chunk (lane % 4) ^ ((row >> 1) & 3) (row = q * 16 + a_r, and
+  // q * 16 does not change (row >> 1) & 3).
+  const int a_kf = FULL ? (((lane & 3) ^ ((a_r >> 1) & 3)) << 2) : a_k;
+  const float* a_ptr = P.A + (m0 + a_r) * P.lda + kt0 * SK + a_kf;
   const float* b_ptr = P.Bm + (kt0 * SK + b_k) * P.ldb + gc;
 
-  auto load_full = [&]() {
+  // Full tiles, the next K stage into the stage at dst: instruction q of A
+  // fills rows q*16 .. q*16+15 (1 KiB), instruction q of B k rows q*4 .. q*4+3.
+  auto issue_direct = [&](float* dst) {
 #pragma unroll
-    for (int q = 0; q < kAQ; ++q) put4(ra, q, *reinterpret_cast<const float4*>(a_ptr + q * 16 * P.lda));
+    for (int q = 0; q < kAQ; ++q) load_lds16(a_ptr + q * 16 * P.lda, dst + q * 256);
 #pragma unroll
-    for (int q = 0; q < kBQ; ++q) put4(rb, q, *reinterpret_cast<const float4*>(b_ptr + q * 4 * P.ldb));
+    for (int q = 0; q < kBQ; ++q) load_lds16(b_ptr + q * 4 * P.ldb, dst + b_off(0, 0) + q * 256);
     a_ptr += SK;
     b_ptr += SK * P.ldb;
   };
+
   // K stage kt of this wave (zeros past the wave's range, K, M or N).
   auto load_checked = [&](int64_t kt) {
     const bool in = kt < kt1;
@@ -334,12 +363,11 @@ __global__ __launch_bounds__(64 * kNarrowKG) void narrow_kernel(const GemmParams
       }
     }
   };
-  auto store_stage = [&](int buf) {
+  auto store_stage = [&](float* dst) {
 #pragma unroll
-    for (int q = 0; q < kAQ; ++q) a_vec4(buf, q * 16 + a_r, a_k) = get4(ra, q);
+    for (int q = 0; q < kAQ; ++q) *reinterpret_cast<float4*>(dst + a_off(q * 16 + a_r, a_k)) = get4(ra, q);
 #pragma unroll
-    for (int q = 0; q < kBQ; ++q)
-      *reinterpret_cast<float4*>(&b_at(buf, q * 4 + b_k, b_c)) = get4(rb, q);
+    for (int q = 0; q < kBQ; ++q) *reinterpret_cast<float4*>(dst + b_off(q * 4 + b_k, b_c)) = get4(rb, q);
   };
 
   // Step mode: thread t finishes the (row, channel) pairs t, t + kThreads,
@@ -365,42 +393,64 @@ __global__ __launch_bounds__(64 * kNarrowKG) void narrow_kernel(const GemmParams
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  if constexpr (FULL) load_full(); else load_checked(kt0);
-  store_stage(0);
-  __syncthreads();
-  for (int it = 0; it < iters; ++it) {
-    const int buf = it & 1;
-    if (it + 1 < iters) {
-      if constexpr (FULL) load_full(); else load_checked(kt0 + it + 1);
-    }
-    // K order within a stage: MFMA s (s < SK / 2) takes k = s from lanes
-    // 0..31 and k = SK / 2 + s from lanes 32..63 (the same for A and B), so a
-    // lane reads its A values of all SK / 2 MFMAs with 16-byte reads.
+  // The MFMAs of the stage at cur.  K order within a stage: MFMA s (s < SK /
+  // 2) takes k = s from lanes 0..31 and k = SK / 2 + s from lanes 32..63 (the
+  // same for A and B), so a lane reads its A values of all SK / 2 MFMAs with
+  // 16-byte reads.
+  auto mfma_stage = [&](const float* cur) {
     float a[RI][SK / 2];
 #pragma unroll
     for (int i = 0; i < RI; ++i)
 #pragma unroll
       for (int q = 0; q < SK / 8; ++q) {
-        const float4 v = a_vec4(buf, i * 32 + ml, kl * (SK / 2) + 4 * q);
+        const float4 v = *reinterpret_cast<const float4*>(cur + a_off(i * 32 + ml, kl * (SK / 2) + 4 * q));
         a[i][4 * q + 0] = v.x; a[i][4 * q + 1] = v.y; a[i][4 * q + 2] = v.z; a[i][4 * q + 3] = v.w;
       }
 #pragma unroll
     for (int s = 0; s < SK / 2; ++s) {
       float b[2];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) b[j] = b_at(buf, kl * (SK / 2) + s, j * 32 + ml);
+      for (int j = 0; j < 2; ++j) b[j] = cur[b_off(kl * (SK / 2) + s, j * 32 + ml)];
 #pragma unroll
       for (int i = 0; i < RI; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][s], b[j], acc[i][j], 0, 0, 0);
     }
-    if (it + 1 < iters) store_stage(buf ^ 1);
-    __syncthreads();
-  }
+  };
+  // Full tiles: the direct loads of the next stage into nxt (when issue), then
+  // the MFMAs of the stage at cur.  The restrict qualifiers state that the two
+  // stages do not overlap, so the compiler reads cur without first waiting for
+  // the loads into nxt; wait_stage() after the stage makes them visible.
+  auto full_stage = [&](const float* __restrict__ cur, float* __restrict__ nxt, bool issue) {
+    if (issue) issue_direct(nxt);
+    mfma_stage(cur);
+  };
 
-  // The waves' sums: red[g][row][c] over the staging LDS (free after the
-  // loop's last barrier).
+  // Each wave stages and reads only its own buffers, so the K loop needs no
+  // workgroup barrier: a wave's LDS accesses take effect in its issue order,
+  // and its direct loads are waited for (vmcnt) before it reads them.
+  if constexpr (FULL) {
+    issue_direct(stage_at(0));
+    wait_stage();
+  } else {
+    load_checked(kt0);
+    store_stage(stage_at(0));
+  }
+  for (int it = 0; it < iters; ++it) {
+    const int buf = it & 1;
+    if constexpr (FULL) {
+      full_stage(stage_at(buf), stage_at(buf ^ 1), it + 1 < iters);
+      wait_stage();
+    } else {
+      if (it + 1 < iters) load_checked(kt0 + it + 1);
+      mfma_stage(stage_at(buf));
+      if (it + 1 < iters) store_stage(stage_at(buf ^ 1));
+    }
+  }
+  __syncthreads();  // every wave is done with the staging LDS
+
+  // The waves' sums: red[g][row][c] over the staging LDS.
   float* red = smem;
   constexpr int kRedWave = TM * G::kLdR;
 #pragma unroll
@@ -527,7 +577,7 @@ hipError_t launch_small_m(const GemmParams& P, hipStream_t stream) {
 
 template <int MODE, int TM>
 void launch_narrow_tm(bool full, uint32_t tiles, const GemmParams& P, hipStream_t stream) {
-  const dim3 grid{tiles}, block{uint32_t(Narrow<TM>::kThreads)};
+  const dim3 grid{tiles}, block{uint32_t(Narrow<TM, true>::kThreads)};
   if (full)
     hipLaunchKernelGGL((narrow_kernel<MODE, TM, true>), grid, block, 0, stream, P);
   else
