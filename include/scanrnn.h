@@ -25,7 +25,7 @@
  * - All tensor pointers are DEVICE pointers; the caller owns every buffer,
  *   including the workspace.  The library keeps no pointer after a call
  *   returns and holds no global mutable state except a thread-local error
- *   string.
+ *   string and the look-back poll bound (scanrnn_set_lookback_spin_limit).
  * - Tensors are row-major, innermost (feature) dimension fastest; a [B,T,D]
  *   tensor is B*T rows of D elements.  Pointers must be aligned to their
  *   element size; wider alignment (8 or 16 bytes) lets the library use
@@ -228,6 +228,21 @@ sr_status minmax_scan_backward(int64_t B, int64_t T, int64_t D,
 
 /* Text of the last non-OK status returned on this thread ("" if none). */
 const char* scanrnn_last_error(void);
+
+/* Polls of a predecessor's unwritten look-back word after which a scan tile
+ * gives up: it marks its workspace (see scanrnn_workspace_status) and
+ * carries NaN for that channel instead of waiting longer (minGRU results are
+ * NaN from there on; MinMax's min and max drop a NaN operand, so there only
+ * the status shows it).  The default bound is never reached in normal
+ * operation (predecessors are running, and publish within microseconds). */
+#define SCANRNN_LOOKBACK_SPIN_LIMIT (1u << 20)
+
+/* Lowers the bound above for scans launched afterwards by this process (all
+ * threads; launches already enqueued keep theirs).  Meant for tests of the
+ * timeout path: 0 gives up at the first unwritten word met.  polls above
+ * SCANRNN_LOOKBACK_SPIN_LIMIT: SR_ERR_INVALID_ARGUMENT, nothing changed.
+ * Pass SCANRNN_LOOKBACK_SPIN_LIMIT to restore the default. */
+sr_status scanrnn_set_lookback_spin_limit(uint32_t polls);
 
 /* Waits for `stream`, then reports whether a scan that used `workspace` since
  * its last reset gave up waiting for a predecessor chunk (a bounded wait that

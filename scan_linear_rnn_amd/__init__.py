@@ -47,6 +47,7 @@ SR_ERR_HIP = 4
 SR_ERR_LOOKBACK_TIMEOUT = 5
 SR_F32 = 0
 SR_BF16 = 1
+LOOKBACK_SPIN_LIMIT = 1 << 20  # SCANRNN_LOOKBACK_SPIN_LIMIT
 
 EXPORTED = (
     "mingru_forward_workspace_size",
@@ -63,6 +64,7 @@ EXPORTED = (
     "minmax_scan_backward_workspace_size",
     "minmax_scan_backward",
     "scanrnn_last_error",
+    "scanrnn_set_lookback_spin_limit",
     "scanrnn_workspace_status",
     "scanrnn_version",
 )
@@ -118,6 +120,8 @@ def _load() -> ctypes.CDLL:
                                          sz, vp]
     lib.scanrnn_last_error.restype = ctypes.c_char_p
     lib.scanrnn_last_error.argtypes = []
+    lib.scanrnn_set_lookback_spin_limit.restype = i32
+    lib.scanrnn_set_lookback_spin_limit.argtypes = [ctypes.c_uint32]
     lib.scanrnn_workspace_status.restype = i32
     lib.scanrnn_workspace_status.argtypes = [vp, vp]
     lib.scanrnn_version.restype = ctypes.c_char_p
@@ -488,6 +492,15 @@ def minmax_scan_backward(r, s, x0, x_out, dx, dx_last=None, workspace=None):
                                    ws.numel(), _stream(r.device))
     _check("minmax_scan_backward", st)
     return dr, ds, dx0
+
+
+def set_lookback_spin_limit(polls: int) -> None:
+    """Bound on the polls of an unwritten look-back word for scans launched
+    afterwards (process-wide; at most LOOKBACK_SPIN_LIMIT, the default).  For
+    tests of the timeout path."""
+    if not 0 <= polls <= LOOKBACK_SPIN_LIMIT:
+        raise ValueError(f"polls must be in [0, {LOOKBACK_SPIN_LIMIT}] (got {polls})")
+    _check("scanrnn_set_lookback_spin_limit", _lib.scanrnn_set_lookback_spin_limit(polls))
 
 
 def workspace_status(ws: torch.Tensor) -> int:

@@ -5,6 +5,7 @@
 // validation failure, which also lets the checks run on a machine without a
 // GPU.
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -15,6 +16,7 @@ namespace sr {
 
 namespace {
 thread_local char g_last_error[512] = "";
+std::atomic<uint32_t> g_spin_limit{SCANRNN_LOOKBACK_SPIN_LIMIT};
 
 bool mul_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_mul_overflow(a, b, out); }
 
@@ -262,6 +264,8 @@ sr_status step_impl(int64_t B, int64_t D_in, int64_t D_h, int64_t D_out, const f
 
 }  // namespace
 
+uint32_t lookback_spin_limit() { return g_spin_limit.load(std::memory_order_relaxed); }
+
 sr_status fail(sr_status code, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
@@ -458,6 +462,14 @@ sr_status minmax_scan_backward(int64_t B, int64_t T, int64_t D, const float* r, 
   rq.workspace = workspace;
   rq.stream = as_stream(stream);
   return launch_scan_backward(rq);
+}
+
+sr_status scanrnn_set_lookback_spin_limit(uint32_t polls) {
+  g_last_error[0] = '\0';
+  SR_REQUIRE(polls <= SCANRNN_LOOKBACK_SPIN_LIMIT, "spin limit %u above the default %u", polls,
+             (unsigned)SCANRNN_LOOKBACK_SPIN_LIMIT);
+  g_spin_limit.store(polls, std::memory_order_relaxed);
+  return SR_OK;
 }
 
 sr_status scanrnn_workspace_status(const void* workspace, void* stream) {

@@ -203,6 +203,7 @@ sr_status launch_fused_forward(const FusedRequest& rq) {
   P.status = reinterpret_cast<uint32_t*>(ws) + 1;
   P.state = reinterpret_cast<uint64_t*>(ws + eng::kHeaderBytes);
   P.window = eng::kWindowTiles;
+  P.spin_limit = lookback_spin_limit();
   P.rate = rq.decay_rate;
   P.gap = rq.delta_t;
   P.log1p_gap = rq.log1p_delta;

@@ -14,6 +14,11 @@ namespace sr {
 // returns `code`.
 sr_status fail(sr_status code, const char* fmt, ...);
 
+// Polls of an unwritten look-back word after which a scan gives up (marks
+// the workspace, publishes NaN): process-wide, SCANRNN_LOOKBACK_SPIN_LIMIT
+// unless scanrnn_set_lookback_spin_limit lowered it.
+uint32_t lookback_spin_limit();
+
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 constexpr size_t kAlign = 256;

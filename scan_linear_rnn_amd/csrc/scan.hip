@@ -347,6 +347,7 @@ sr_status launch_scan(const ScanRequest& rq) {
   P.status = reinterpret_cast<uint32_t*>(ws) + 1;
   P.state = reinterpret_cast<uint64_t*>(ws + kHeaderBytes);
   P.window = lookback_window(P.n_chains);
+  P.spin_limit = lookback_spin_limit();
   P.rate = rq.decay_rate;
   P.gap = rq.delta_t;
   P.log1p_gap = rq.log1p_delta;

@@ -292,6 +292,7 @@ sr_status launch_scan_backward(const BackwardRequest& rq) {
   P.status = reinterpret_cast<uint32_t*>(ws) + 1;
   P.state = reinterpret_cast<uint64_t*>(ws + kHeaderBytes);
   P.window = kWindowTiles;
+  P.spin_limit = lookback_spin_limit();
   Q.in0 = rq.in0;
   Q.in1 = rq.in1;
   Q.ld_in = rq.ld_in;

@@ -13,7 +13,6 @@ namespace eng {
 constexpr uint32_t kTagEmpty = 0xFFFFFFFFu;
 constexpr uint32_t kTagState = 0xFFFFFFFEu;
 constexpr uint32_t kCanonNaN = 0x7FC00000u;
-constexpr uint32_t kSpinLimit = 1u << 20;
 constexpr size_t kHeaderBytes = 256;
 constexpr int kWaves = 12;           // waves per workgroup
 constexpr int kElemsPerLane = 24;    // N * V: maps each lane keeps in registers
@@ -170,6 +169,7 @@ struct ScanParams {
   uint32_t* status;   // header word 1: timeout flag
   uint64_t* state;    // [n_tchunks][B][D] look-back words
   int window;         // look-back words fetched per tile in the first round trip, 1..kWindowTiles
+  uint32_t spin_limit;  // polls of an unwritten look-back word before giving up
   // Time decay of the carried state (minGRU only; unused when rate is null).
   const float* rate;     // [D] per-channel decay rate
   const float* gap;      // [B,T] gap preceding each token
@@ -234,7 +234,7 @@ __device__ float lookback_serial(const ScanParams& P, int64_t tchunk, int64_t b,
       break;
     }
     // Tile top - stop has not published yet: poll its word.
-    if (++spins > kSpinLimit) {
+    if (++spins > P.spin_limit) {
       __hip_atomic_store(P.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       return __uint_as_float(kCanonNaN);
     }

@@ -157,6 +157,18 @@ def test_minmax_rejects_bad_arguments():
     assert f(2, 8, 4, FAKE, FAKE, FAKE, FAKE, None, None, big, None) == sr.SR_ERR_INVALID_ARGUMENT
 
 
+def test_spin_limit_setter_bounds():
+    text = open(HEADER).read()
+    assert "#define SCANRNN_LOOKBACK_SPIN_LIMIT (1u << 20)" in text
+    assert sr.LOOKBACK_SPIN_LIMIT == 1 << 20
+    assert lib.scanrnn_set_lookback_spin_limit(sr.LOOKBACK_SPIN_LIMIT + 1) == sr.SR_ERR_INVALID_ARGUMENT
+    assert b"above the default" in lib.scanrnn_last_error()
+    assert lib.scanrnn_set_lookback_spin_limit(0) == sr.SR_OK
+    assert lib.scanrnn_set_lookback_spin_limit(sr.LOOKBACK_SPIN_LIMIT) == sr.SR_OK
+    with pytest.raises(ValueError):
+        sr.set_lookback_spin_limit(-1)
+
+
 def test_status_requires_workspace():
     assert lib.scanrnn_workspace_status(None, None) == sr.SR_ERR_INVALID_ARGUMENT
 
