@@ -31,7 +31,8 @@ contract: a per-event gap decays the carried state at the token boundary).
 The minGRU equations themselves (h_t = (1 - z_t) h_{t-1} + z_t g(p_t),
 z = sigma(k), g(x) = x + 1/2 for x >= 0 else sigma(x), [k, p] = x W_in, the
 identities log(1 - z) = -softplus(k)) are not printed on the pages; they are
-the benchmark spec of the method and are written out here as given.
+the published minGRU definition (Feng et al., "Were RNNs All We Needed?",
+2024), which the profile's layer implements, written out here as given.
 
 Parity status of each function is listed in its module docstring.
 """

@@ -1,8 +1,9 @@
 """minGRU layer, run as its plain sequential definition in float64.
 
-The method (as stated for the log-space minGRU layer of the minGRU-pytorch
-profile; the equations are the benchmark spec, the pages name only the
-layer, its log-space form and its two modes):
+The method (the log-space minGRU layer of the minGRU-pytorch profile; the
+equations are the published minGRU definition, Feng et al., "Were RNNs All We
+Needed?", 2024 -- the pages name only the layer, its log-space form and its
+two modes):
 
     [k_t | p_t] = x_t W_in            k = first D_h columns, p = the next D_h
     z_t         = sigma(k_t)

@@ -14,7 +14,7 @@ def pytest_configure(config):
 
 def pytest_collection_modifyitems(config, items):
     # A GPU test must not silently fall back anywhere: when no GPU is
-    # present it is skipped here, and on a GPU machine it runs the HIP library.
+    # present it is skipped here, and with a GPU it runs the HIP library.
     try:
         import torch
         have_gpu = torch.cuda.is_available()
