@@ -201,3 +201,43 @@ def test_step_batch_sizes(B):
         assert metrics.max_abs_rel(host64(h), h_ref) < TOL_F32
         assert metrics.y_rel_err(host64(y_t), y_ref, h_ref, W_out) < TOL_F32
         h_ref = host64(h)
+
+
+@pytest.mark.parametrize("B,D_in,D_h,decayed,path", [
+    (5, 40, 96, False, "FMA path (<= 16 rows)"),
+    (100, 72, 130, False, "narrow 32-row tiles, ragged"),
+    (256, 256, 2048, False, "narrow 64-row tiles, full"),
+    (256, 256, 2048, True, "narrow 64-row tiles, full, decayed"),
+    (700, 1024, 256, False, "128-row tiles with K split over workgroups"),
+    (700, 1024, 256, True, "128-row tiles with K split, decayed"),
+])
+def test_step_in_place_on_every_path(B, D_in, D_h, decayed, path):
+    """h_next may be h_prev: every product path reads each carried state
+    before the same workgroup (or the split-K reduction) overwrites it.  The
+    in-place step equals the out-of-place one bit for bit, and the oracle."""
+    say(f"in-place step B={B} D_in={D_in} D_h={D_h} decayed={decayed}: {path}")
+    rng = np.random.default_rng([1710, B, D_h, int(decayed)])
+    W_in = (rng.standard_normal((D_in, 2 * D_h)) / np.sqrt(D_in)).astype(np.float32)
+    x_t = rng.standard_normal((B, D_in)).astype(np.float32)
+    h0 = rng.standard_normal((B, D_h)).astype(np.float32)
+    lam = (10.0 ** rng.uniform(-3, 0, D_h)).astype(np.float32)
+    dt = rng.exponential(1.0, B).astype(np.float32)
+    Wi, xd = dev(W_in), dev(x_t)
+
+    def step(h_prev, h_next):
+        if decayed:
+            return sr.mingru_step_decayed(xd, Wi, None, h_prev=h_prev, h_next=h_next,
+                                          decay_rate=dev(lam), delta_t=dev(dt))
+        return sr.mingru_step(xd, Wi, None, h_prev=h_prev, h_next=h_next)
+
+    _, apart = step(dev(h0), None)
+    h = dev(h0)
+    _, same = step(h, h)
+    assert same.data_ptr() == h.data_ptr()
+    assert torch.equal(h, apart)
+    if decayed:
+        from oracle import decay
+        _, h_ref = decay.step(x_t, W_in, lam, dt, None, h0)
+    else:
+        _, h_ref = mingru.step(x_t, W_in, None, h0)
+    assert metrics.max_abs_rel(host64(h), h_ref) < TOL_F32
