@@ -256,16 +256,24 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 }  // namespace
 
 ScanGeometry choose_geometry(const ScanRequest& rq) {
-  // Two channels per lane when the data allows it: 128-channel tiles keep
-  // many independent chains along T (so few tiles of a chain are in flight
-  // at once and the look-back window reaches a finished tile), with 4-byte
-  // bf16 / 8-byte fp32 accesses that still cover whole cache lines per wave.
+  // Two channels per lane when the data allows it, the 128-channel tiles pad
+  // no more than 64-channel ones, and they still leave at least 32 chains
+  // (batch rows x channel tiles): 4-byte bf16 / 8-byte fp32 accesses cover
+  // whole cache lines per wave.  With fewer chains, about 512 resident tiles
+  // put dozens of tiles of each chain in flight at once, and nearly every
+  // tile waits on predecessors that are still loading (serial look-back,
+  // ~11 tiles deep at 8 chains); one channel per lane doubles the chains and
+  // halves that depth, which outweighs its 128-byte row segments.  Measured
+  // (bf16, one launch): 1 x 65536 x 1024 128.3 -> 120.9 us, 8 x 65536 x 256
+  // 213.7 -> 204.4 us; equal at 32 chains (4 x 65536 x 1024), and 48 chains
+  // are better with two channels per lane.
   const size_t esz = rq.in_dtype == SR_BF16 ? 2 : 4;
   int V = 1;
   const bool v2 = rq.D % 2 == 0 && rq.ld_in % 2 == 0 && aligned(rq.in0, esz * 2) &&
                   aligned(rq.in1, esz * 2) && aligned(rq.out, 8);
   const int64_t tiles_2 = (rq.D + 127) / 128, tiles_1 = (rq.D + 63) / 64;
-  if (v2 && tiles_2 * 128 <= tiles_1 * 64) V = 2;
+  constexpr int64_t kMinChains = 32;
+  if (v2 && tiles_2 * 128 <= tiles_1 * 64 && rq.B * tiles_2 >= kMinChains) V = 2;
   ScanGeometry g;
   g.V = V;
   g.N = kElemsPerLane / V;

@@ -30,6 +30,10 @@ def _inputs(B, T, D, seed, k_mean=0.0, k_std=1.5, with_h0=True):
     (2, 2, 3, False),          # D with no vector width
     (1, 333, 130, True),       # D = 2 * 65: ragged lanes
     (4, 2500, 64, False),
+    # At least 32 chains (batch rows x 128-channel tiles): two channels per
+    # lane; the shapes above take one channel per lane.
+    (32, 1000, 200, True),     # ragged T and D
+    (16, 700, 1000, True),     # D = 1000: the last 128-channel tile part full
 ])
 def test_scan_f32_matches_oracle(B, T, D, with_h0):
     say(f"scan f32 B={B} T={T} D={D} h0={with_h0}")
@@ -41,8 +45,9 @@ def test_scan_f32_matches_oracle(B, T, D, with_h0):
     assert np.array_equal(host64(last), host64(y)[:, -1, :])
 
 
-def test_scan_bf16_long_memory_statistics():
-    B, T, D = 2, 4096, 1024
+@pytest.mark.parametrize("B", [2, 4])  # 16 chains (one channel per lane), 32 (two)
+def test_scan_bf16_long_memory_statistics(B):
+    T, D = 4096, 1024
     say(f"scan bf16 long-memory B={B} T={T} D={D}")
     cfg = synth.CONFIGS[synth.SCAN]
     k32 = synth.normal_bt(synth.SCAN, "k", B, T, D, cfg["k_mean"], cfg["k_std"])
@@ -57,9 +62,10 @@ def test_scan_bf16_long_memory_statistics():
     assert err < 1e-5  # the arithmetic itself is fp32: regressions show long before 2e-2
 
 
-def test_scan_kp_halves_of_one_buffer():
-    B, T, D = 2, 700, 96
-    say("scan ld_kp != D_h")
+@pytest.mark.parametrize("B", [2, 32])  # one / two channels per lane
+def test_scan_kp_halves_of_one_buffer(B):
+    T, D = 700, 96
+    say(f"scan ld_kp != D_h, B={B}")
     rng = np.random.default_rng(77)
     kp = rng.standard_normal((B, T, 2 * D)).astype(np.float32)
     t = dev(kp)
