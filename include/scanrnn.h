@@ -98,8 +98,9 @@ sr_status mingru_forward(int64_t B, int64_t T, int64_t D_in, int64_t D_h, int64_
                          float* y, float* h_last,
                          void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of workspace mingru_step needs (none up to 512 streams, where the
- * K range is split inside each workgroup). */
+/* Bytes of workspace mingru_step needs: none up to 512 streams, nor up to
+ * 4096 streams while D_in and D_h are at most 1024 (the K range is then
+ * split inside each workgroup); otherwise split-K partial sums. */
 size_t mingru_step_workspace_size(int64_t B, int64_t D_in, int64_t D_h, int64_t D_out);
 
 /*

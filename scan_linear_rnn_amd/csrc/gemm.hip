@@ -205,6 +205,15 @@ __global__ __launch_bounds__(kSmallThreads) void small_m_kernel(const GemmParams
 // apply the step update.
 constexpr int kNarrowCols = 64;
 constexpr int kNarrowMaxM = 512;
+// Up to kNarrowWideMaxM rows the narrow tiles also replace a 128 x 128
+// tiling that would leave CUs idle (fewer than 512 tiles; it would split K
+// across workgroups and add a reduction launch) when K is at most
+// kNarrowWideMaxK; with deeper K the split 128 x 128 tiles are faster.
+// Measured (one process): layer forward B=2 T=1024 D=512 78 -> 54 us,
+// B=2 T=2048 D=512 100 -> 94 us, step B=2048 D=512 67 -> 42 us, step B=1024
+// D=1024 81 -> 68 us; with K = 2048 (B=2 T=1024 D=2048) 449 -> 456 us.
+constexpr int kNarrowWideMaxM = 4096;
+constexpr int kNarrowWideMaxK = 1024;
 constexpr int kNarrowKG = 8;  // waves (K groups) per workgroup
 constexpr int kNarrowSK = 16; // K per pipeline stage
 
@@ -520,15 +529,19 @@ __global__ void reduce_step_kernel(const GemmParams P, int S) {
 
 }  // namespace
 
-int gemm_splits(int64_t M, int64_t N, int64_t K, bool step) {
-  // Enough workgroups for two per CU on a 256-CU part, each K slice at
-  // least 256 deep; small problems (the single-token step) split K, large
-  // ones (whole-sequence projections) do not.  Products of at most
-  // kNarrowMaxM rows take the FMA path or the narrow tiles, which split K
-  // inside the workgroup.
-  if (M <= kNarrowMaxM || K < 2 * 256) return 1;  // nothing worth splitting (and K = 0 has no slices)
-  const int64_t tiles = ((M + BM - 1) / BM) * (step ? (N / 2 + BN / 2 - 1) / (BN / 2)
-                                                    : (N + BN - 1) / BN);
+namespace {
+
+// Tiles of the 128 x 128 tiling (step mode: 64 channels per tile).
+int64_t tiles_128(int64_t M, int64_t N, bool step) {
+  return ((M + BM - 1) / BM) * (step ? (N / 2 + BN / 2 - 1) / (BN / 2) : (N + BN - 1) / BN);
+}
+
+// K slices of the 128 x 128 tiling: enough workgroups for two per CU on a
+// 256-CU part, each K slice at least 256 deep; small problems split K,
+// large ones (whole-sequence projections) do not.
+int splits_128(int64_t M, int64_t N, int64_t K, bool step) {
+  if (K < 2 * 256) return 1;  // nothing worth splitting (and K = 0 has no slices)
+  const int64_t tiles = tiles_128(M, N, step);
   if (tiles <= 0 || tiles >= 512) return 1;
   int64_t s = (512 + tiles - 1) / tiles;
   const int64_t by_k = K / 256;
@@ -538,6 +551,18 @@ int gemm_splits(int64_t M, int64_t N, int64_t K, bool step) {
   // Slices are whole multiples of the K step.
   const int64_t k_split = ((K + s - 1) / s + BK - 1) / BK * BK;
   return int((K + k_split - 1) / k_split);
+}
+
+// Products that run on the narrow tiles (at most kSmallM rows: the FMA path).
+bool narrow_applies(int64_t M, int64_t N, int64_t K, bool step) {
+  if (M <= kNarrowMaxM) return true;
+  return M <= kNarrowWideMaxM && K <= kNarrowWideMaxK && tiles_128(M, N, step) < 512;
+}
+
+}  // namespace
+
+int gemm_splits(int64_t M, int64_t N, int64_t K, bool step) {
+  return narrow_applies(M, N, K, step) ? 1 : splits_128(M, N, K, step);
 }
 
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, bool step) {
@@ -628,7 +653,7 @@ sr_status launch_mode(int mode, GemmParams P, float* ws, hipStream_t stream, boo
     if (e != hipSuccess) return fail(SR_ERR_HIP, "small GEMM launch: %s", hipGetErrorString(e));
     return SR_OK;
   }
-  if (P.M <= kNarrowMaxM)
+  if (narrow_applies(P.M, P.ncols, P.K, mode == kStep))
     return mode == kPlain ? launch_narrow<kPlain>(P, stream, check_only)
                           : launch_narrow<kStep>(P, stream, check_only);
   const int64_t cols_per_tile = mode == kPlain ? BN : BN / 2;

@@ -57,8 +57,8 @@ def test_workspace_sizes():
     assert lib.minmax_scan_workspace_size(8, 32768, 192) > 0
     assert lib.mingru_forward_workspace_size(-1, 4, 4, 4, 4, 0, 0) == 0
     # The single-token step splits K inside the workgroup up to 512 streams
-    # (no workspace); larger batches split it across workgroups, whose
-    # partial sums need workspace; tiny shapes need none.
+    # (no workspace); larger batches with K > 1024 split it across
+    # workgroups, whose partial sums need workspace; tiny shapes need none.
     assert lib.mingru_step_workspace_size(256, 2048, 2048, 2048) == 0
     assert lib.mingru_step_workspace_size(512, 2048, 2048, 2048) == 0
     assert lib.mingru_step_workspace_size(1024, 2048, 2048, 2048) >= 1024 * 4096 * 4 * 2
@@ -79,9 +79,13 @@ def test_workspace_sizes_with_zero_and_small_dims():
         assert lib.minmax_scan_workspace_size(B, T, D_h) >= 0
         assert lib.mingru_scan_backward_workspace_size(B, T, D_h) >= 0
     # No input features: the input product has K = 0 and needs no partial
-    # sums (with K = 1024 it splits); D_out = 0 leaves no output product.
+    # sums; up to 4096 rows with K <= 1024 the K range is split inside each
+    # workgroup; with K = 2048 it is split across workgroups. D_out = 0
+    # leaves no output product.
     assert lib.mingru_step_workspace_size(1024, 0, 512, 0) == 0
-    assert lib.mingru_step_workspace_size(1024, 1024, 512, 0) > 0
+    assert lib.mingru_step_workspace_size(1024, 1024, 512, 0) == 0
+    assert lib.mingru_step_workspace_size(1024, 2048, 512, 0) > 0
+    assert lib.mingru_step_workspace_size(8192, 1024, 64, 0) > 0  # few 128-row tiles past 4096 rows
     plain = lib.mingru_forward_workspace_size(4, 1000, 0, 256, 256, 1, 0)
     staged = 4 * 1000 * 2 * 256 * 4   # the [k|p] staging alone
     assert staged <= plain < staged + (1 << 20)

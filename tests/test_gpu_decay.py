@@ -216,9 +216,9 @@ def test_full_size_b8_t65536_d1024_decayed_sampled():
 
 
 def test_decayed_step_over_many_streams():
-    """1024 streams: the step's products split K across workgroups, and the
-    reduction kernel applies the decayed update."""
-    B, D_in, D_h = 1024, 512, 512
+    """1024 streams with D_in = 2048: the input product splits K across
+    workgroups, and the reduction kernel applies the decayed update."""
+    B, D_in, D_h = 1024, 2048, 512
     say("decayed step B=1024")
     assert sr.raw_library().mingru_step_workspace_size(B, D_in, D_h, D_h) > 0
     rng = np.random.default_rng(1204)

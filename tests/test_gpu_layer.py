@@ -208,8 +208,9 @@ def test_step_batch_sizes(B):
     (100, 72, 130, False, "narrow 32-row tiles, ragged"),
     (256, 256, 2048, False, "narrow 64-row tiles, full"),
     (256, 256, 2048, True, "narrow 64-row tiles, full, decayed"),
-    (700, 1024, 256, False, "128-row tiles with K split over workgroups"),
-    (700, 1024, 256, True, "128-row tiles with K split, decayed"),
+    (700, 1024, 256, False, "narrow tiles above 512 rows (K <= 1024)"),
+    (700, 2048, 256, False, "128-row tiles with K split over workgroups"),
+    (700, 2048, 256, True, "128-row tiles with K split, decayed"),
 ])
 def test_step_in_place_on_every_path(B, D_in, D_h, decayed, path):
     """h_next may be h_prev: every product path reads each carried state

@@ -1,6 +1,7 @@
-"""GPU parity of the products with 17..512 rows (the step over a batch of
-streams, short forwards): narrow tiles of 64 or 32 rows x 64 columns, the K
-range split over groups of waves inside the workgroup.  Shapes cover both
+"""GPU parity of the products on narrow tiles (17..512 rows, and up to 4096
+rows when a 128 x 128 tiling would leave CUs idle and K <= 1024: the step
+over a batch of streams, short forwards): tiles of 64 or 32 rows x 64
+columns, the K range split over groups of waves inside the workgroup.  Shapes cover both
 tile heights, ragged rows, columns, channels and K, K shorter than one
 group's share, operands that allow no 16-byte loads, and full tiles."""
 
@@ -28,6 +29,8 @@ def _weights(rng, D_in, D_h, D_out):
     (480, 512, 1024, 1024),   # 64-row tiles, last row tile half full
     (512, 256, 2048, 2048),   # 64-row tiles, every tile full
     (64, 2048, 64, 48),       # a long K over few tiles
+    (1000, 700, 333, 129),    # above 512 rows (K <= 1024): ragged rows, odd D_h
+    (2048, 512, 512, 512),    # above 512 rows, every tile full
 ])
 def test_narrow_step_matches_oracle(B, D_in, D_h, D_out):
     say(f"narrow step B={B} D_in={D_in} D_h={D_h} D_out={D_out}")
@@ -74,6 +77,7 @@ def test_narrow_step_decayed_and_repeatable():
     (3, 100, 96, 96, 200),    # projections of 300 rows, ragged columns
     (1, 512, 64, 256, 64),    # 512 rows, full tiles
     (7, 19, 5, 70, 33),       # K = 5 and 70 (not multiples of 16)
+    (3, 1000, 96, 300, 200),  # 3000 rows: narrow tiles replace an underfilled 128-row tiling
 ])
 def test_narrow_forward_projections(B, T, D_in, D_h, D_out):
     say(f"narrow forward B={B} T={T} D_in={D_in} D_h={D_h} D_out={D_out}")
