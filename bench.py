@@ -352,6 +352,32 @@ def leg_layer(torch, sr, synth, workload, steps):
                                      steps, 3)
     res = dict(B=B, T=T, D=D, forward_ms=wall / steps * 1e3, forward_launch_ms=mean_ms,
                elements_per_s=B * T * D / (wall / steps))
+    # The same forward captured once in a HIP graph and replayed (inputs,
+    # output and workspace fixed): what a caller bound by launch overhead
+    # would run.
+    ws = torch.empty(sr.raw_library().mingru_forward_workspace_size(B, T, D, D, D, 1, 1),
+                     dtype=torch.uint8, device="cuda")
+    y = torch.empty(B, T, D, device="cuda")
+
+    def fwd():
+        sr.mingru_forward(x, W_in, W_out=W_out, workspace=ws, out=y)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fwd()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fwd()
+    graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    res["graph_forward_ms"] = (time.perf_counter() - t0) / steps * 1e3
+    del graph
     xs = [x[:, t].contiguous() for t in range(T)]
 
     def loop():
