@@ -20,6 +20,16 @@ otherwise the carried state passes through.
     dL/dr_t = Gamma_{t+1} [r_t selected],  dL/ds_t = Gamma_{t+1} [s_t selected]
     dL/dx_0 = [step 0 passes its state] Gamma_1
 
+Time-decayed minGRU (the decay contract of the "Your first delta model"
+tutorial, Step 5 "Adding time decay": the carried state is scaled by
+gamma_t = exp(-min(lambda_d gap_t, 1e4)) at the token boundary, as in
+oracle/decay.py): the step's coefficient becomes c_t = a_t gamma_t, so
+    G_t      = dh_t + c_{t+1} G_{t+1}
+    dL/dk_t  = G_t z_t (1 - z_t) (g(p_t) - gamma_t h_{t-1})
+    dL/dp_t  = G_t z_t g'(p_t)
+    dL/dh_0  = c_1 G_1
+with the rates and gaps held fixed (no gradient for them).
+
 Pinned by: fp64 torch.autograd through independently written forward loops,
 central finite differences, and closed forms (tests/test_oracle_grad.py).
 """
@@ -61,6 +71,35 @@ def mingru_scan_backward(k, p, h0, dh, dh_last=None):
         dk[:, t] = G * z[:, t] * a[:, t] * (gp[:, t] - h_prev[:, t])
         dp[:, t] = G * z[:, t] * g_prime(p[:, t])
         G = a[:, t] * G  # the part of dL/dh_{t-1} that flows through step t
+    return dk, dp, G
+
+
+def mingru_decayed_scan_backward(k, p, decay_rate, delta_t, h0, dh, dh_last=None,
+                                 log1p_delta=False):
+    """Returns (dk, dp, dh0) of the time-decayed scan (oracle/decay.py) for
+    L = sum_t <dh_t, h_t> + <dh_last, h_T>; decay_rate [D], delta_t [B, T]."""
+    from . import decay
+    k = _f64(k)
+    p = _f64(p)
+    dh = _f64(dh)
+    B, T, D = k.shape
+    z = scalar.sigmoid(k)
+    a = scalar.sigmoid(-k)
+    gp = scalar.g(p)
+    gam = decay.gamma(decay_rate, delta_t, log1p_delta)  # [B, T, D]
+    h = np.zeros((B, D)) if h0 is None else _f64(h0).copy()
+    h_prev = np.empty((B, T, D))
+    for t in range(T):
+        h_prev[:, t] = h
+        h = a[:, t] * (gam[:, t] * h) + z[:, t] * gp[:, t]
+    dk = np.empty((B, T, D))
+    dp = np.empty((B, T, D))
+    G = np.zeros((B, D)) if dh_last is None else _f64(dh_last).copy()
+    for t in range(T - 1, -1, -1):
+        G = dh[:, t] + G
+        dk[:, t] = G * z[:, t] * a[:, t] * (gp[:, t] - gam[:, t] * h_prev[:, t])
+        dp[:, t] = G * z[:, t] * g_prime(p[:, t])
+        G = a[:, t] * gam[:, t] * G
     return dk, dp, G
 
 

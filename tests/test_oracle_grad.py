@@ -211,3 +211,138 @@ def test_minmax_autograd_pin_catches_wrong_selection():
     # swap the roles of r and s in the routing
     dr, ds, dx0 = grad.minmax_scan_backward(r, s, x0, dx, dl)
     assert _rel(ds, tr.grad.numpy()) > 1e-3 and _rel(dr, ts.grad.numpy()) > 1e-3
+
+
+# ---------------------------------------------------------------- decayed
+
+def _decay_inputs(seed, B=2, T=9, D=3):
+    k, p, h0, dh, dl = _mingru_inputs(seed, B=B, T=T, D=D)
+    rng = np.random.default_rng([1020, seed])
+    lam = 10.0 ** rng.uniform(-2, 0, D)
+    gap = rng.exponential(1.0, (B, T))
+    return k, p, h0, dh, dl, lam, gap
+
+
+def _torch_decayed_loss(k, p, h0, dh, dl, lam, gap):
+    # Written independently of oracle/decay.py: gamma = exp(-min(lambda gap, 1e4)).
+    z = torch.sigmoid(k)
+    gp = torch.where(p >= 0, p + 0.5, torch.sigmoid(p))
+    gam = torch.exp(-torch.clamp(gap[:, :, None] * lam[None, None, :], max=1e4))
+    h = h0
+    loss = 0.0
+    for t in range(k.shape[1]):
+        h = (1 - z[:, t]) * (gam[:, t] * h) + z[:, t] * gp[:, t]
+        loss = loss + (dh[:, t] * h).sum()
+    return loss + (dl * h).sum()
+
+
+def autograd_decayed(k, p, h0, dh, dl, lam, gap):
+    tk, tp, th = (torch.tensor(v, requires_grad=True) for v in (k, p, h0))
+    _torch_decayed_loss(tk, tp, th, torch.tensor(dh), torch.tensor(dl), torch.tensor(lam),
+                        torch.tensor(gap)).backward()
+    return tk.grad.numpy(), tp.grad.numpy(), th.grad.numpy()
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_decayed_backward_matches_autograd(seed):
+    k, p, h0, dh, dl, lam, gap = _decay_inputs(seed)
+    ours = grad.mingru_decayed_scan_backward(k, p, lam, gap, h0, dh, dl)
+    ref = autograd_decayed(k, p, h0, dh, dl, lam, gap)
+    for a, b in zip(ours, ref):
+        assert _rel(a, b) < 1e-12
+
+
+def test_decayed_backward_finite_differences():
+    k, p, h0, dh, dl, lam, gap = _decay_inputs(5, B=1, T=6, D=2)
+
+    def loss(k_, p_, h0_):
+        with torch.no_grad():
+            return float(_torch_decayed_loss(torch.tensor(k_), torch.tensor(p_), torch.tensor(h0_),
+                                             torch.tensor(dh), torch.tensor(dl), torch.tensor(lam),
+                                             torch.tensor(gap)))
+    dk, dp, dh0 = grad.mingru_decayed_scan_backward(k, p, lam, gap, h0, dh, dl)
+    eps = 1e-6
+    for arr, g in ((k, dk), (p, dp), (h0, dh0)):
+        for idx in np.ndindex(arr.shape):
+            if arr is p and abs(arr[idx]) < 1e-3:
+                continue
+            plus, minus = arr.copy(), arr.copy()
+            plus[idx] += eps
+            minus[idx] -= eps
+            args_p = [plus if a is arr else a for a in (k, p, h0)]
+            args_m = [minus if a is arr else a for a in (k, p, h0)]
+            fd = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+            assert abs(fd - g[idx]) < 1e-7 * max(1.0, abs(g[idx])), (idx, fd, g[idx])
+
+
+def test_decayed_backward_reduces_to_undecayed():
+    # lambda = 0 or every gap 0: gamma = 1 exactly, the same arithmetic.
+    k, p, h0, dh, dl, lam, gap = _decay_inputs(7)
+    plain = grad.mingru_scan_backward(k, p, h0, dh, dl)
+    for lam_, gap_ in ((np.zeros_like(lam), gap), (lam, np.zeros_like(gap))):
+        dec = grad.mingru_decayed_scan_backward(k, p, lam_, gap_, h0, dh, dl)
+        for a, b in zip(dec, plain):
+            assert np.array_equal(a, b)
+
+
+def test_decayed_backward_saturating_gap_cuts_the_gradient():
+    # A gap of 1e6 at step t* (gamma = 0 there): nothing before t* feels the
+    # gradients from t* on, and dh0 vanishes when t* is the first step.
+    k, p, h0, dh, dl, lam, gap = _decay_inputs(8, T=12)
+    ts = 5
+    gap = gap.copy()
+    gap[:, ts] = 1e6
+    dk, dp, dh0 = grad.mingru_decayed_scan_backward(k, p, lam, gap, h0, dh, dl)
+    dh2 = dh.copy()
+    dh2[:, ts:] *= -3.0
+    dk2, dp2, dh02 = grad.mingru_decayed_scan_backward(k, p, lam, gap, h0, dh2, 5.0 * dl)
+    assert np.array_equal(dk[:, :ts], dk2[:, :ts]) and np.array_equal(dp[:, :ts], dp2[:, :ts])
+    assert np.array_equal(dh0, dh02)
+    gap[:, 0] = 1e6
+    assert np.all(grad.mingru_decayed_scan_backward(k, p, lam, gap, h0, dh, dl)[2] == 0.0)
+
+
+def test_decayed_backward_log1p_gaps():
+    k, p, h0, dh, dl, lam, gap = _decay_inputs(9)
+    u = gap
+    a = grad.mingru_decayed_scan_backward(k, p, lam, np.expm1(u), h0, dh, dl, log1p_delta=True)
+    b = grad.mingru_decayed_scan_backward(k, p, lam, u, h0, dh, dl)
+    for x, y in zip(a, b):
+        assert _rel(x, y) < 1e-13
+
+
+def _mutant_decayed(k, p, lam, gap, h0, dh, dl, undecayed_dk=False, next_gamma=False,
+                    no_gamma_in_g=False):
+    """Planted mistakes: h_{t-1} undecayed in dk; gamma_{t+1} used where
+    gamma_t belongs; G propagated without the decay."""
+    from oracle import decay
+    z = scalar.sigmoid(k)
+    a = scalar.sigmoid(-k)
+    gp = scalar.g(p)
+    gam = decay.gamma(lam, gap)
+    B, T, D = k.shape
+    h = h0.copy()
+    h_prev = np.empty((B, T, D))
+    for t in range(T):
+        h_prev[:, t] = h
+        h = a[:, t] * (gam[:, t] * h) + z[:, t] * gp[:, t]
+    dk = np.empty((B, T, D))
+    G = dl.copy()
+    for t in range(T - 1, -1, -1):
+        G = dh[:, t] + G
+        gt = gam[:, min(t + 1, T - 1)] if next_gamma else gam[:, t]
+        dk[:, t] = G * z[:, t] * a[:, t] * (gp[:, t] - (1.0 if undecayed_dk else gt) * h_prev[:, t])
+        G = a[:, t] * (1.0 if no_gamma_in_g else gam[:, t]) * G
+    return dk, G
+
+
+@pytest.mark.parametrize("kw", [dict(undecayed_dk=True), dict(next_gamma=True),
+                                dict(no_gamma_in_g=True)])
+def test_decayed_autograd_pin_catches_mistakes(kw):
+    k, p, h0, dh, dl, lam, gap = _decay_inputs(3)
+    dk_ref, _, dh0_ref = autograd_decayed(k, p, h0, dh, dl, lam, gap)
+    dk, dh0 = _mutant_decayed(k, p, lam, gap, h0, dh, dl, **kw)
+    assert _rel(dk, dk_ref) > 1e-6 or _rel(dh0, dh0_ref) > 1e-6
+    # and the unmutated arithmetic passes the same check
+    dk0, dh00 = _mutant_decayed(k, p, lam, gap, h0, dh, dl)
+    assert _rel(dk0, dk_ref) < 1e-12 and _rel(dh00, dh0_ref) < 1e-12
