@@ -282,6 +282,38 @@ def leg_scan_decay(torch, sr, synth, steps, warmup):
     return res
 
 
+def leg_scan_backward_decay(torch, sr, synth, steps, warmup):
+    """Backward of the decayed scan at the headline shape: the plain
+    backward's 20 bytes per element plus one gap per (b, t) and one rate per
+    channel."""
+    cfg = synth.CONFIGS[synth.SCAN]
+    B, T, D = cfg["B"], cfg["T"], cfg["D"]
+    log(f"[bench] decayed scan backward B={B} T={T} D={D}")
+    kb = synth.device_normal(synth.SCAN, "k", (B, T, D), cfg["k_mean"], cfg["k_std"], torch.bfloat16)
+    pb = synth.device_normal(synth.SCAN, "p", (B, T, D), cfg["p_mean"], cfg["p_std"], torch.bfloat16)
+    h0 = synth.device_normal(synth.SCAN, "h0", (B, D))
+    rate = torch.from_numpy(synth.decay_rates(synth.SCAN, D)).cuda()
+    gap = torch.from_numpy(synth.gaps(synth.SCAN, B, T)).cuda()
+    h = sr.mingru_forward_decayed(k=kb, p=pb, h0=h0, decay_rate=rate, delta_t=gap)
+    dh = torch.empty_like(h).normal_(0.0, 1.0)
+    ws = torch.empty(sr.raw_library().mingru_scan_backward_workspace_size(B, T, D),
+                     dtype=torch.uint8, device="cuda")
+    wall, mean_ms, _ = time_launches(
+        torch, lambda: sr.mingru_scan_backward_decayed(kb, pb, h, dh, h0=h0, workspace=ws,
+                                                       decay_rate=rate, delta_t=gap),
+        steps, warmup)
+    if sr.workspace_status(ws) != 0:
+        raise RuntimeError("decayed scan backward: look-back expired")
+    n = B * T * D
+    alg = n * 20 + B * T * 4 + D * 4 + 3 * B * D * 4
+    res = dict(B=B, T=T, D=D, launch_ms_mean=mean_ms, elements_per_s=n / (wall / steps),
+               achieved_GBps=alg / (mean_ms * 1e-3) / 1e9,
+               frac_of_hbm_peak=alg / (mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS)
+    del kb, pb, h, dh, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def leg_minmax_backward(torch, sr, synth, steps, warmup):
     """Backward of the MinMax scan: reads r, s, x_out, dx, writes dr, ds
     (fp32): 24 algorithmic bytes per element."""
@@ -433,8 +465,8 @@ def main():
     # A fresh process reaches steady clocks only after a few hundred ms of
     # sustained load (measured: the first ~100 launches run 3-5% slower).
     ap.add_argument("--warmup", type=int, default=1000)
-    ap.add_argument("--legs", default="scan,minmax,scan_bwd,minmax_bwd,scan_decay,decode,layer_d512,"
-                                      "layer_d16,minmax_step,copy")
+    ap.add_argument("--legs", default="scan,minmax,scan_bwd,minmax_bwd,scan_decay,scan_decay_bwd,"
+                                      "decode,layer_d512,layer_d16,minmax_step,copy")
     ap.add_argument("--cpu-steps", type=int, default=65536,
                     help="sequence prefix the CPU oracle baseline runs over (0 = skip)")
     ap.add_argument("--decode-steps", type=int, default=4096)
@@ -469,6 +501,9 @@ def main():
                                                                   args.warmup)
     if "scan_decay" in legs:
         extra["decayed_b8_t65536_d1024"] = leg_scan_decay(torch, sr, synth, args.steps, args.warmup)
+    if "scan_decay_bwd" in legs:
+        extra["decayed_backward_b8_t65536_d1024"] = leg_scan_backward_decay(
+            torch, sr, synth, args.steps, args.warmup)
     if "layer_d512" in legs:
         extra["layer_b2_t1024_d512"] = leg_layer(torch, sr, synth, synth.LAYER, 10)
     if "layer_d16" in legs:

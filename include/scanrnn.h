@@ -214,6 +214,26 @@ sr_status mingru_scan_backward(int64_t B, int64_t T, int64_t D,
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Backward pass of the time-decayed minGRU scan (mingru_forward_decayed
+ * without projections; decay contract of the delta tutorial, Step 5
+ * "Adding time decay").  With gamma_t = exp(-min(decay_rate_d * gap_t, 1e4))
+ * and c_t = (1 - z_t) gamma_t:
+ *     dk_t = G_t z_t (1 - z_t) (g(p_t) - gamma_t h_{t-1}),  dp_t = G_t z_t g'(p_t),
+ *     dh0  = c_1 G_1,   with  G_t = dh_t + c_{t+1} G_{t+1}.
+ * decay_rate [D], delta_t [B,T] and log1p_delta as in mingru_forward_decayed
+ * (the rates and gaps get no gradient); everything else and the workspace
+ * size (mingru_scan_backward_workspace_size) as in mingru_scan_backward.
+ */
+sr_status mingru_scan_backward_decayed(int64_t B, int64_t T, int64_t D,
+                                       const void* k, const void* p, int64_t ld_kp,
+                                       sr_dtype kp_dtype,
+                                       const float* decay_rate, const float* delta_t,
+                                       int log1p_delta,
+                                       const float* h0, const float* h, const float* dh,
+                                       const float* dh_last, float* dk, float* dp, float* dh0,
+                                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Backward pass of the MinMax scan (minmaxrnc page, "Key properties": the
  * gradient through the state path neither vanishes nor explodes -- it is
  * routed, unchanged, to the operand each step selects).  Gradients dx on

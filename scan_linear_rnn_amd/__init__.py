@@ -31,6 +31,7 @@ __all__ = [
     "mingru_step_decayed",
     "minmax_scan",
     "mingru_scan_backward",
+    "mingru_scan_backward_decayed",
     "minmax_scan_backward",
     "library_path",
     "ScanRNNError",
@@ -61,6 +62,7 @@ EXPORTED = (
     "minmax_step",
     "mingru_scan_backward_workspace_size",
     "mingru_scan_backward",
+    "mingru_scan_backward_decayed",
     "minmax_scan_backward_workspace_size",
     "minmax_scan_backward",
     "scanrnn_last_error",
@@ -115,6 +117,9 @@ def _load() -> ctypes.CDLL:
     lib.mingru_scan_backward.restype = i32
     lib.mingru_scan_backward.argtypes = [i64, i64, i64, vp, vp, i64, i32, vp, vp, vp, vp, vp, vp,
                                          vp, vp, sz, vp]
+    lib.mingru_scan_backward_decayed.restype = i32
+    lib.mingru_scan_backward_decayed.argtypes = [i64, i64, i64, vp, vp, i64, i32, vp, vp, i32, vp,
+                                                 vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.minmax_scan_backward.restype = i32
     lib.minmax_scan_backward.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                          sz, vp]
@@ -442,6 +447,19 @@ def mingru_scan_backward(k, p, h, dh, h0=None, dh_last=None, workspace=None):
     ``h`` is the forward output, ``dh`` [B,T,D] the gradient on it and
     ``dh_last`` [B,D] the gradient on the returned final state.  Returns
     (dk, dp, dh0) in fp32 (dh0 is None when h0 is None)."""
+    return _scan_backward(k, p, h, dh, h0, dh_last, workspace, None)
+
+
+def mingru_scan_backward_decayed(k, p, h, dh, h0=None, dh_last=None, workspace=None, *,
+                                 decay_rate, delta_t, log1p_delta=False):
+    """``mingru_scan_backward`` of the time-decayed scan (``decay_rate`` [D],
+    ``delta_t`` [B,T] as given to ``mingru_forward_decayed``; they get no
+    gradient)."""
+    return _scan_backward(k, p, h, dh, h0, dh_last, workspace,
+                          (decay_rate, delta_t, log1p_delta, None))
+
+
+def _scan_backward(k, p, h, dh, h0, dh_last, workspace, decay):
     if k.dtype not in (torch.float32, torch.bfloat16) or p.dtype != k.dtype:
         raise TypeError("k and p must both be float32 or both bfloat16")
     if k.dim() != 3 or p.shape != k.shape:
@@ -464,11 +482,19 @@ def mingru_scan_backward(k, p, h, dh, h0=None, dh_last=None, workspace=None):
     dh0 = torch.empty((B, D), dtype=torch.float32, device=k.device) if h0 is not None else None
     nbytes = _lib.mingru_scan_backward_workspace_size(B, T, D)
     ws = _use_workspace(workspace, nbytes, k.device)
-    st = _lib.mingru_scan_backward(B, T, D, _ptr(k), _ptr(p), k.stride(1),
-                                   SR_BF16 if k.dtype == torch.bfloat16 else SR_F32, _ptr(h0),
-                                   _ptr(h), _ptr(dh), _ptr(dh_last), _ptr(dk), _ptr(dp), _ptr(dh0),
-                                   _ptr(ws), ws.numel(), _stream(k.device))
-    _check("mingru_scan_backward", st)
+    dtype = SR_BF16 if k.dtype == torch.bfloat16 else SR_F32
+    if decay is None:
+        st = _lib.mingru_scan_backward(B, T, D, _ptr(k), _ptr(p), k.stride(1), dtype, _ptr(h0),
+                                       _ptr(h), _ptr(dh), _ptr(dh_last), _ptr(dk), _ptr(dp),
+                                       _ptr(dh0), _ptr(ws), ws.numel(), _stream(k.device))
+        _check("mingru_scan_backward", st)
+    else:
+        rate, gap, log1p, _ = _decay_args(decay, D, (B, T), k.device)
+        st = _lib.mingru_scan_backward_decayed(B, T, D, _ptr(k), _ptr(p), k.stride(1), dtype,
+                                               _ptr(rate), _ptr(gap), log1p, _ptr(h0), _ptr(h),
+                                               _ptr(dh), _ptr(dh_last), _ptr(dk), _ptr(dp),
+                                               _ptr(dh0), _ptr(ws), ws.numel(), _stream(k.device))
+        _check("mingru_scan_backward_decayed", st)
     return dk, dp, dh0
 
 

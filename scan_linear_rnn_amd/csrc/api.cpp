@@ -266,6 +266,52 @@ sr_status step_impl(int64_t B, int64_t D_in, int64_t D_h, int64_t D_out, const f
 
 uint32_t lookback_spin_limit() { return g_spin_limit.load(std::memory_order_relaxed); }
 
+namespace {
+
+sr_status mingru_backward_impl(int64_t B, int64_t T, int64_t D, const void* k, const void* p,
+                               int64_t ld_kp, sr_dtype kp_dtype, const float* h0, const float* h,
+                               const float* dh, const float* dh_last, float* dk, float* dp,
+                               float* dh0, void* workspace, size_t workspace_bytes, void* stream,
+                               const Decay* dec) {
+  SR_REQUIRE(B >= 0 && T >= 0 && D >= 0, "sizes must be non-negative (B=%lld T=%lld D=%lld)",
+             (long long)B, (long long)T, (long long)D);
+  int64_t n, span;
+  SR_REQUIRE(prod3(B, T, D, &n), "tensor sizes overflow int64");
+  SR_REQUIRE(kp_dtype == SR_F32 || kp_dtype == SR_BF16, "kp_dtype %d unsupported", int(kp_dtype));
+  SR_REQUIRE(ld_kp >= D, "ld_kp (%lld) must be >= D (%lld)", (long long)ld_kp, (long long)D);
+  SR_REQUIRE(prod3(B, T, ld_kp, &span), "k/p extent overflows int64");
+  SR_REQUIRE(n == 0 || (k && p && h && dh && dk && dp), "k, p, h, dh, dk and dp are required");
+  const size_t esz = kp_dtype == SR_BF16 ? 2 : 4;
+  SR_REQUIRE(aligned(k, esz) && aligned(p, esz), "k and p must be aligned to their element size");
+  SR_REQUIRE(aligned(h0, 4) && aligned(h, 4) && aligned(dh, 4) && aligned(dh_last, 4) &&
+                 aligned(dk, 4) && aligned(dp, 4) && aligned(dh0, 4),
+             "fp32 pointers must be 4-byte aligned");
+  if (dec != nullptr) {
+    sr_status st = check_decay(*dec, n > 0 ? D : 0, n > 0 ? B * T : 0);
+    if (st != SR_OK) return st;
+  }
+  sr_status st = check_workspace(workspace, workspace_bytes,
+                                 mingru_scan_backward_workspace_size(B, T, D));
+  if (st != SR_OK) return st;
+  BackwardRequest rq{};
+  rq.op = ScanOp::kMinGRU;
+  rq.in_dtype = kp_dtype;
+  rq.B = B; rq.T = T; rq.D = D;
+  rq.in0 = k; rq.in1 = p; rq.ld_in = ld_kp;
+  rq.fwd = h; rq.fwd0 = h0; rq.grad = dh; rq.grad_last = dh_last;
+  rq.d0 = dk; rq.d1 = dp; rq.dinit = dh0;
+  if (dec != nullptr && n > 0) {
+    rq.decay_rate = dec->rate;
+    rq.delta_t = dec->delta_t;
+    rq.log1p_delta = dec->log1p_delta;
+  }
+  rq.workspace = workspace;
+  rq.stream = as_stream(stream);
+  return launch_scan_backward(rq);
+}
+
+}  // namespace
+
 sr_status fail(sr_status code, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
@@ -406,32 +452,21 @@ sr_status mingru_scan_backward(int64_t B, int64_t T, int64_t D, const void* k, c
                                float* dh0, void* workspace, size_t workspace_bytes,
                                void* stream) {
   g_last_error[0] = '\0';
-  SR_REQUIRE(B >= 0 && T >= 0 && D >= 0, "sizes must be non-negative (B=%lld T=%lld D=%lld)",
-             (long long)B, (long long)T, (long long)D);
-  int64_t n, span;
-  SR_REQUIRE(prod3(B, T, D, &n), "tensor sizes overflow int64");
-  SR_REQUIRE(kp_dtype == SR_F32 || kp_dtype == SR_BF16, "kp_dtype %d unsupported", int(kp_dtype));
-  SR_REQUIRE(ld_kp >= D, "ld_kp (%lld) must be >= D (%lld)", (long long)ld_kp, (long long)D);
-  SR_REQUIRE(prod3(B, T, ld_kp, &span), "k/p extent overflows int64");
-  SR_REQUIRE(n == 0 || (k && p && h && dh && dk && dp), "k, p, h, dh, dk and dp are required");
-  const size_t esz = kp_dtype == SR_BF16 ? 2 : 4;
-  SR_REQUIRE(aligned(k, esz) && aligned(p, esz), "k and p must be aligned to their element size");
-  SR_REQUIRE(aligned(h0, 4) && aligned(h, 4) && aligned(dh, 4) && aligned(dh_last, 4) &&
-                 aligned(dk, 4) && aligned(dp, 4) && aligned(dh0, 4),
-             "fp32 pointers must be 4-byte aligned");
-  sr_status st = check_workspace(workspace, workspace_bytes,
-                                 mingru_scan_backward_workspace_size(B, T, D));
-  if (st != SR_OK) return st;
-  BackwardRequest rq{};
-  rq.op = ScanOp::kMinGRU;
-  rq.in_dtype = kp_dtype;
-  rq.B = B; rq.T = T; rq.D = D;
-  rq.in0 = k; rq.in1 = p; rq.ld_in = ld_kp;
-  rq.fwd = h; rq.fwd0 = h0; rq.grad = dh; rq.grad_last = dh_last;
-  rq.d0 = dk; rq.d1 = dp; rq.dinit = dh0;
-  rq.workspace = workspace;
-  rq.stream = as_stream(stream);
-  return launch_scan_backward(rq);
+  return mingru_backward_impl(B, T, D, k, p, ld_kp, kp_dtype, h0, h, dh, dh_last, dk, dp, dh0,
+                              workspace, workspace_bytes, stream, nullptr);
+}
+
+sr_status mingru_scan_backward_decayed(int64_t B, int64_t T, int64_t D, const void* k,
+                                       const void* p, int64_t ld_kp, sr_dtype kp_dtype,
+                                       const float* decay_rate, const float* delta_t,
+                                       int log1p_delta, const float* h0, const float* h,
+                                       const float* dh, const float* dh_last, float* dk, float* dp,
+                                       float* dh0, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
+  g_last_error[0] = '\0';
+  const Decay dec{decay_rate, delta_t, log1p_delta, nullptr};
+  return mingru_backward_impl(B, T, D, k, p, ld_kp, kp_dtype, h0, h, dh, dh_last, dk, dp, dh0,
+                              workspace, workspace_bytes, stream, &dec);
 }
 
 sr_status minmax_scan_backward(int64_t B, int64_t T, int64_t D, const float* r, const float* s,

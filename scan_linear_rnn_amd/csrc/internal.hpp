@@ -109,6 +109,10 @@ struct BackwardRequest {
   float* d0;            // dk or dr [B,T,D]
   float* d1;            // dp or ds [B,T,D]
   float* dinit;         // dh0 or dx0 [B,D] or null
+  // Time decay of the carried state (minGRU only; none when decay_rate is null).
+  const float* decay_rate;  // [D]
+  const float* delta_t;     // [B,T]
+  int log1p_delta;
   void* workspace;
   hipStream_t stream;
 };

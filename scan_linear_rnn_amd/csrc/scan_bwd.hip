@@ -9,6 +9,11 @@
 //   minGRU : G_t = a_{t+1} G_{t+1} + dh_t      (a = 1 - z = sigma(-k))
 //            dk_t = G_t z_t a_t (g(p_t) - h_{t-1}),  dp_t = G_t z_t g'(p_t),
 //            dh_0 = a_1 G_1
+//            With time decay (the delta tutorial's "Adding time decay": the
+//            carried state is scaled by gamma_t = exp(-lambda_d gap_t) before
+//            token t's write) a_t becomes a_t gamma_t in G and dh_0, and
+//            h_{t-1} becomes gamma_t h_{t-1} in dk_t; rates and gaps get no
+//            gradient.
 //   MinMax : Gamma_{t+1} = c_{t+1} Gamma_{t+2} + dx_{t+1}, c in {0, 1} the
 //            "state passes through" indicator of the step; dr_t / ds_t get
 //            Gamma_{t+1} where r_t / s_t was selected, dx_0 = c_0 Gamma_1.
@@ -46,6 +51,9 @@ struct BwdParams {
   float* d0;            // dk / dr  [B,T,D]
   float* d1;            // dp / ds  [B,T,D]
   float* dinit;         // dh0 / dx0 [B,D] or null
+  const float* rate;    // time decay (minGRU): [D] per-channel rate
+  const float* gap;     // [B,T] gap preceding each token
+  int log1p_gap;        // gaps compressed with log1p first
 };
 
 __device__ __forceinline__ void sig_pair(float k, float& z, float& a) {
@@ -77,7 +85,7 @@ enum Kind { kMinGRU = 0, kMinMax = 1 };
 // step n, are t_n = t_hi - n; loads are clamped into [0, T) and addressed
 // from the lowest row any of them touches, so every buffer offset is
 // non-negative and small.
-template <int KIND, typename TIn, int V, int N, int W>
+template <int KIND, typename TIn, int V, int N, int W, bool kDecay = false>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(kBwdWavesPerSimd)))
 void scan_backward_kernel(const BwdParams Q) {
   using R = Raw<TIn, V>;
@@ -130,6 +138,35 @@ void scan_backward_kernel(const BwdParams Q) {
     if (KIND == kMinMax || i < N) fw[i] = RF::load(rf, vf, soff(KIND == kMinMax ? t_hi - i : t_hi - 1 - i, f_row));
     if (i < N) gr[i] = RF::load(rg, vf, soff(t_hi - i, f_row));
   }
+  // Time decay: -rate * log2(e) for the lane's channels, and lane i holding
+  // the gap of time t_hi + 1 - i (i = 0 .. N; rows clamped into [0, T), and
+  // only the in-range ones are used), so that step n reads the gaps of its
+  // following step (lane n) and of itself (lane n + 1) with readlane.
+  float nrate[V];
+  float gap_l = 0.0f;
+  if constexpr (kDecay) {
+    const rsrc_t rr = make_rsrc(Q.rate + tl.d0, (P.D - tl.d0) * 4);
+    float rv[V];
+    RF::unpack(RF::load(rr, lane * V * 4, 0), rv);
+#pragma unroll
+    for (int c = 0; c < V; ++c) nrate[c] = rv[c] * kNegLog2e;
+    const int64_t gt = t_hi + 1 - lane;
+    const int64_t grow = gt < 0 ? 0 : (gt > T - 1 ? T - 1 : gt);
+    const rsrc_t rgap = make_rsrc(Q.gap + tl.b * T, T * 4);
+    gap_l = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rgap, int(grow * 4), 0, 0));
+    if (Q.log1p_gap) gap_l = log1pf(gap_l);
+  }
+  // The decay factor of step (t_hi + 1 - i) for each of the lane's channels.
+  auto decay_at = [&](int i, float (&gam)[V]) {
+#pragma unroll
+    for (int c = 0; c < V; ++c) gam[c] = 1.0f;
+    if constexpr (kDecay) {
+      const float gp = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gap_l), i));
+#pragma unroll
+      for (int c = 0; c < V; ++c) gam[c] = __builtin_amdgcn_exp2f(nrate[c] * gp);
+    }
+  };
+
   // The forward state before step 0 (for t = 0).
   float init_state[V];
 #pragma unroll
@@ -148,13 +185,14 @@ void scan_backward_kernel(const BwdParams Q) {
     RF::unpack(gr[n], gv);
     float coef[V];
     if (KIND == kMinGRU) {
-      float kn[V];
+      float kn[V], gam[V];
       R::unpack(i0[n], kn);  // k_{t+1}
+      decay_at(n, gam);      // gamma_{t+1}
 #pragma unroll
       for (int c = 0; c < V; ++c) {
         float z, a;
         sig_pair(kn[c], z, a);
-        coef[c] = a;
+        coef[c] = a * gam[c];
       }
     } else {
       float rn[V], sn[V], xn[V];
@@ -200,13 +238,14 @@ void scan_backward_kernel(const BwdParams Q) {
     for (int c = 0; c < V; ++c) G[c] = MinGRUOp::apply(e[n][c], G[c]);
     float o0v[V], o1v[V], pass_or_a[V];
     if (KIND == kMinGRU) {
-      float kt[V], pt[V], hp[V];
+      float kt[V], pt[V], hp[V], gam[V];
       R::unpack(i0[n + 1], kt);
       R::unpack(i1[n], pt);
       RF::unpack(fw[n], hp);
+      decay_at(n + 1, gam);  // gamma_t
 #pragma unroll
       for (int c = 0; c < V; ++c) {
-        const float h_prev = t == 0 ? init_state[c] : hp[c];
+        const float h_prev = (t == 0 ? init_state[c] : hp[c]) * gam[c];
         float z, a, g, gs;
         sig_pair(kt[c], z, a);
         g_and_slope(pt[c], g, gs);
@@ -214,7 +253,7 @@ void scan_backward_kernel(const BwdParams Q) {
         // of the normal range (|k| near 87), and G z a would go subnormal.
         o0v[c] = ((z * a) * (g - h_prev)) * G[c];
         o1v[c] = G[c] * z * gs;
-        pass_or_a[c] = a;
+        pass_or_a[c] = a * gam[c];
       }
     } else {
       float rt[V], st[V], xt[V];
@@ -241,12 +280,13 @@ void scan_backward_kernel(const BwdParams Q) {
   }
 }
 
-template <int KIND, typename TIn, int V>
+template <int KIND, typename TIn, int V, bool kDecay = false>
 hipError_t launch_bwd_v(const BwdParams& Q, hipStream_t stream) {
   constexpr int N = kBwdElemsPerLane / V;
+  static_assert(N + 1 <= 64, "one lane per gap of the run");
   const int64_t n_blocks = Q.core.n_chains * Q.core.n_tchunks;
-  hipLaunchKernelGGL((scan_backward_kernel<KIND, TIn, V, N, kBwdWaves>), dim3(uint32_t(n_blocks)),
-                     dim3(64 * kBwdWaves), 0, stream, Q);
+  hipLaunchKernelGGL((scan_backward_kernel<KIND, TIn, V, N, kBwdWaves, kDecay>),
+                     dim3(uint32_t(n_blocks)), dim3(64 * kBwdWaves), 0, stream, Q);
   return hipGetLastError();
 }
 
@@ -302,12 +342,24 @@ sr_status launch_scan_backward(const BackwardRequest& rq) {
   Q.d0 = rq.d0;
   Q.d1 = rq.d1;
   Q.dinit = rq.dinit;
+  Q.rate = rq.decay_rate;
+  Q.gap = rq.delta_t;
+  Q.log1p_gap = rq.log1p_delta;
+  const bool decay = rq.decay_rate != nullptr;
+  if (decay && rq.op != ScanOp::kMinGRU)
+    return fail(SR_ERR_UNSUPPORTED, "time decay applies to the minGRU scan only");
   sr_status st = reset_workspace(ws, kHeaderBytes + size_t(P.n_tchunks) * size_t(P.B) * size_t(P.D) * 8,
                                  rq.stream);
   if (st != SR_OK) return st;
   hipError_t err;
   if (rq.op == ScanOp::kMinMax)
     err = V == 2 ? launch_bwd_v<kMinMax, float, 2>(Q, rq.stream) : launch_bwd_v<kMinMax, float, 1>(Q, rq.stream);
+  else if (decay && rq.in_dtype == SR_BF16)
+    err = V == 2 ? launch_bwd_v<kMinGRU, uint16_t, 2, true>(Q, rq.stream)
+                 : launch_bwd_v<kMinGRU, uint16_t, 1, true>(Q, rq.stream);
+  else if (decay)
+    err = V == 2 ? launch_bwd_v<kMinGRU, float, 2, true>(Q, rq.stream)
+                 : launch_bwd_v<kMinGRU, float, 1, true>(Q, rq.stream);
   else if (rq.in_dtype == SR_BF16)
     err = V == 2 ? launch_bwd_v<kMinGRU, uint16_t, 2>(Q, rq.stream)
                  : launch_bwd_v<kMinGRU, uint16_t, 1>(Q, rq.stream);

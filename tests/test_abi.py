@@ -173,6 +173,23 @@ def test_spin_limit_setter_bounds():
         sr.set_lookback_spin_limit(-1)
 
 
+def test_decayed_backward_rejects_bad_arguments():
+    f = lib.mingru_scan_backward_decayed
+    big = 1 << 30
+
+    def call(**kw):
+        a = dict(rate=FAKE, gap=FAKE, log1p=0, k=FAKE, p=FAKE2, ws=FAKE)
+        a.update(kw)
+        return f(2, 8, 4, a["k"], a["p"], 4, sr.SR_F32, a["rate"], a["gap"], a["log1p"], None,
+                 FAKE, FAKE, None, FAKE, FAKE, None, a["ws"], big, None)
+    assert call(rate=None) == sr.SR_ERR_INVALID_ARGUMENT
+    assert b"decay_rate" in lib.scanrnn_last_error()
+    assert call(gap=None) == sr.SR_ERR_INVALID_ARGUMENT
+    assert call(log1p=2) == sr.SR_ERR_INVALID_ARGUMENT
+    assert call(rate=ctypes.c_void_p(0x10002)) == sr.SR_ERR_INVALID_ARGUMENT
+    assert call(ws=None) == sr.SR_ERR_INVALID_ARGUMENT
+
+
 def test_status_requires_workspace():
     assert lib.scanrnn_workspace_status(None, None) == sr.SR_ERR_INVALID_ARGUMENT
 
