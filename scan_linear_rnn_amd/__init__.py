@@ -25,6 +25,7 @@ import torch
 
 __all__ = [
     "MinGRU",
+    "mingru_scan",
     "mingru_forward",
     "mingru_forward_decayed",
     "mingru_step",
@@ -532,6 +533,45 @@ def set_lookback_spin_limit(polls: int) -> None:
 def workspace_status(ws: torch.Tensor) -> int:
     """Synchronises the current stream and returns the workspace status code."""
     return _lib.scanrnn_workspace_status(_ptr(ws), _stream(ws.device))
+
+
+class _Scan(torch.autograd.Function):
+    """The minGRU scan (k, p [, h0]) -> h, differentiable: the forward is the
+    scan-only mingru_forward[_decayed], the backward mingru_scan_backward
+    [_decayed] (k, p, h0 get gradients; rates and gaps do not)."""
+
+    @staticmethod
+    def forward(ctx, k, p, h0, decay_rate, delta_t, log1p_delta):
+        if decay_rate is None:
+            h = mingru_forward(k=k, p=p, h0=h0)
+        else:
+            h = mingru_forward_decayed(k=k, p=p, h0=h0, decay_rate=decay_rate, delta_t=delta_t,
+                                       log1p_delta=log1p_delta)
+        ctx.save_for_backward(k, p, h0, h, decay_rate, delta_t)
+        ctx.log1p_delta = log1p_delta
+        return h
+
+    @staticmethod
+    def backward(ctx, dh):
+        k, p, h0, h, decay_rate, delta_t = ctx.saved_tensors
+        dh = dh.contiguous().to(torch.float32)
+        if decay_rate is None:
+            dk, dp, dh0 = mingru_scan_backward(k, p, h, dh, h0=h0)
+        else:
+            dk, dp, dh0 = mingru_scan_backward_decayed(k, p, h, dh, h0=h0, decay_rate=decay_rate,
+                                                       delta_t=delta_t,
+                                                       log1p_delta=ctx.log1p_delta)
+        return dk.to(k.dtype), dp.to(p.dtype), dh0, None, None, None
+
+
+def mingru_scan(k, p, h0=None, *, decay_rate=None, delta_t=None, log1p_delta=False):
+    """The minGRU scan k, p [B,T,D] (fp32 or bf16), h0 [B,D] or None -> h
+    [B,T,D] fp32, differentiable with respect to k, p and h0 through the
+    library's backward kernels (torch autograd only records the call).  With
+    ``decay_rate`` [D] and ``delta_t`` [B,T]: the time-decayed scan."""
+    if (decay_rate is None) != (delta_t is None):
+        raise ValueError("decay_rate and delta_t go together")
+    return _Scan.apply(k, p, h0, decay_rate, delta_t, bool(log1p_delta))
 
 
 class MinGRU:

@@ -134,3 +134,25 @@ def test_full_size_b8_t65536_d1024_decayed_backward_sampled():
         errs.append(max(e))
     say("sampled errors", max(errs))
     assert max(errs) < TOL
+
+
+@pytest.mark.parametrize("decayed", [False, True])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_autograd_scan_uses_the_backward_kernels(decayed, dtype):
+    """sr.mingru_scan under torch autograd: the gradients of k, p and h0 are
+    the backward kernels' results, bit for bit."""
+    B, T, D = 2, 1500, 256
+    say(f"autograd scan decayed={decayed} dtype={dtype}")
+    k, p, h0, dh, _, lam, gap = _case(B, T, D, 3, 300)
+    kd = dev(k).to(dtype).requires_grad_()
+    pd = dev(p).to(dtype).requires_grad_()
+    h0d = dev(h0).requires_grad_()
+    dhd = dev(dh)
+    kw = dict(decay_rate=dev(lam), delta_t=dev(gap)) if decayed else {}
+    h = sr.mingru_scan(kd, pd, h0d, **kw)
+    (h * dhd).sum().backward()
+    fn = sr.mingru_scan_backward_decayed if decayed else sr.mingru_scan_backward
+    with torch.no_grad():
+        ref = fn(kd.detach(), pd.detach(), h.detach(), dhd, h0=h0d.detach(), **kw)
+    assert torch.equal(kd.grad, ref[0].to(dtype)) and torch.equal(pd.grad, ref[1].to(dtype))
+    assert torch.equal(h0d.grad, ref[2])
