@@ -126,6 +126,24 @@ void scan_backward_kernel(const BwdParams Q) {
   const int vin = int(lane * V * esz), vf = lane * V * 4;
   const int64_t in_row = Q.ld_in * esz, f_row = P.D * 4;
 
+  // Time decay: -rate * log2(e) for the lane's channels, and lane i holding
+  // the gap of time t_hi + 1 - i (i = 0 .. N; rows clamped into [0, T), and
+  // only the in-range ones are used), so that step n reads the gaps of its
+  // following step (lane n) and of itself (lane n + 1) with readlane.  Both
+  // are loaded before the step inputs, so that the first step does not wait
+  // for all of those.
+  float nrate[V];
+  float gap_l = 0.0f;
+  typename RF::type rate_raw{};
+  if constexpr (kDecay) {
+    const rsrc_t rr = make_rsrc(Q.rate + tl.d0, (P.D - tl.d0) * 4);
+    rate_raw = RF::load(rr, lane * V * 4, 0);
+    const int64_t gt = t_hi + 1 - lane;
+    const int64_t grow = gt < 0 ? 0 : (gt > T - 1 ? T - 1 : gt);
+    const rsrc_t rgap = make_rsrc(Q.gap + tl.b * T, T * 4);
+    gap_l = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rgap, int(grow * 4), 0, 0));
+  }
+
   // Step inputs.  minGRU: in0 rows t_n+1 .. t_n (k), in1 rows t_n (p),
   // fwd rows t_n - 1 (h_{t-1}).  MinMax: in0/in1 rows t_n+1 .. t_n (r, s),
   // fwd rows t_n .. t_n - 1 (x_{t+1} .. x_t).
@@ -138,23 +156,12 @@ void scan_backward_kernel(const BwdParams Q) {
     if (KIND == kMinMax || i < N) fw[i] = RF::load(rf, vf, soff(KIND == kMinMax ? t_hi - i : t_hi - 1 - i, f_row));
     if (i < N) gr[i] = RF::load(rg, vf, soff(t_hi - i, f_row));
   }
-  // Time decay: -rate * log2(e) for the lane's channels, and lane i holding
-  // the gap of time t_hi + 1 - i (i = 0 .. N; rows clamped into [0, T), and
-  // only the in-range ones are used), so that step n reads the gaps of its
-  // following step (lane n) and of itself (lane n + 1) with readlane.
-  float nrate[V];
-  float gap_l = 0.0f;
   if constexpr (kDecay) {
-    const rsrc_t rr = make_rsrc(Q.rate + tl.d0, (P.D - tl.d0) * 4);
     float rv[V];
-    RF::unpack(RF::load(rr, lane * V * 4, 0), rv);
+    RF::unpack(rate_raw, rv);
 #pragma unroll
     for (int c = 0; c < V; ++c) nrate[c] = rv[c] * kNegLog2e;
-    const int64_t gt = t_hi + 1 - lane;
-    const int64_t grow = gt < 0 ? 0 : (gt > T - 1 ? T - 1 : gt);
-    const rsrc_t rgap = make_rsrc(Q.gap + tl.b * T, T * 4);
-    gap_l = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rgap, int(grow * 4), 0, 0));
-    if (Q.log1p_gap) gap_l = log1pf(gap_l);
+    if (Q.log1p_gap) gap_l = log1pf(gap_l);  // after the input loads are issued
   }
   // The decay factor of step (t_hi + 1 - i) for each of the lane's channels.
   auto decay_at = [&](int i, float (&gam)[V]) {
