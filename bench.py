@@ -22,9 +22,12 @@ carries:
                 workload (every channel; by default the whole sequence,
                 --cpu-steps takes a prefix);
 * legs       -- the other measurements: the MinMax scan, the backward passes
-                of both scans, the time-decayed scan, the decode-style step
-                loop with its prefill, the small layers, the MinMax token
-                loop, and a device copy ceiling.
+                of both scans, the time-decayed scan and its backward, the
+                decode-style step loop with its prefill, the small layers
+                (eagerly and replayed from a HIP graph), the MinMax token
+                loop, and the read+write streaming ceiling (the faster of
+                the device copy and an elementwise kernel with the same
+                traffic; roofline.frac_of_copy_ceiling is relative to it).
 
 Only one GPU is used; --gpus above 1 exits with a message.
 """
