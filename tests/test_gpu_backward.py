@@ -232,3 +232,31 @@ def test_mingru_backward_kp_halves_of_one_buffer():
     errs = _mingru_errors(k, p, h0, dh, None, *got)
     say("errors", errs)
     assert max(errs) < TOL
+
+
+def test_backward_two_chains_across_eight_thousand_tiles():
+    """B=1, T=2^18, D=256: two chains of 4096 tiles each, with ~256 tiles of
+    each chain in flight at once, so nearly every tile walks back through
+    predecessors word by word (the backward's serial look-back) -- against
+    the oracle on sampled channels over the whole sequence."""
+    B, T, D = 1, 1 << 18, 256
+    say(f"backward, two chains: B={B} T={T} D={D}")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1140)
+    k = (torch.empty((B, T, D), device="cuda").normal_(-3.0, 1.0, generator=g)).to(torch.bfloat16)
+    p = torch.empty((B, T, D), device="cuda").normal_(0.0, 1.0, generator=g).to(torch.bfloat16)
+    h0 = torch.empty((B, D), device="cuda").normal_(0.0, 1.0, generator=g)
+    dh = torch.empty((B, T, D), device="cuda").normal_(0.0, 1.0, generator=g)
+    dl = torch.empty((B, D), device="cuda").normal_(0.0, 1.0, generator=g)
+    h = sr.mingru_forward(k=k, p=p, h0=h0)
+    ws = torch.empty(sr.raw_library().mingru_scan_backward_workspace_size(B, T, D),
+                     dtype=torch.uint8, device="cuda")
+    dk, dp, dh0 = sr.mingru_scan_backward(k, p, h, dh, h0=h0, dh_last=dl, workspace=ws)
+    assert sr.workspace_status(ws) == 0
+    ds = torch.as_tensor([0, 127, 128, 255], device="cuda")  # both tiles' edges
+    sl = lambda t: t[0][:, ds].double().cpu().numpy()[None]
+    errs = _mingru_errors(sl(k), sl(p), h0[0][ds].double().cpu().numpy()[None], sl(dh),
+                          dl[0][ds].double().cpu().numpy()[None],
+                          dk[0][:, ds][None], dp[0][:, ds][None], dh0[0][ds][None])
+    say("errors", errs)
+    assert max(errs) < TOL, errs
