@@ -98,3 +98,28 @@ def test_minmax_step_matches_scan_bitwise():
         y = sr.minmax_step(rd[:, t].contiguous(), sd[:, t].contiguous(), x, x_next=x)
         assert y.data_ptr() == x.data_ptr()
         assert torch.equal(x, full[:, t])
+
+
+def test_minmax_three_chains_long_sequence_bitwise():
+    """B=1, T=2^18, D=192: three chains of ~910 tiles, all of them in flight
+    together, so most tiles resolve through long look-back walks.  The
+    forward bit for bit against the oracle; the backward's routing exactly,
+    its routed values (fp32 sums of upstream gradients) within rounding."""
+    from oracle import grad
+    B, T, D = 1, 1 << 18, 192
+    say(f"minmax three chains B={B} T={T} D={D}")
+    r, s, x0 = _inputs(B, T, D, 31)
+    rd, sd, x0d = dev(r), dev(s), dev(x0)
+    out, last = sr.minmax_scan(rd, sd, x0d, return_last=True)
+    ref, ref_last = minmax.scan(r, s, x0)
+    assert metrics.bits_equal(out.cpu().numpy(), ref)
+    assert metrics.bits_equal(last.cpu().numpy(), ref_last)
+    rng = np.random.default_rng(632)
+    dx = rng.standard_normal((B, T, D)).astype(np.float32)
+    dr, ds, dx0 = sr.minmax_scan_backward(rd, sd, x0d, out, dev(dx))
+    rdr, rds, rdx0 = grad.minmax_scan_backward(r, s, x0, dx)
+    assert np.array_equal(dr.cpu().numpy() != 0, rdr != 0)
+    assert np.array_equal(ds.cpu().numpy() != 0, rds != 0)
+    scale = np.abs(dx).sum(axis=1).max()
+    for got, want in ((dr, rdr), (ds, rds), (dx0, rdx0)):
+        assert float(np.max(np.abs(got.cpu().numpy().astype(np.float64) - want))) < 1e-5 * scale
