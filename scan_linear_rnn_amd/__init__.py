@@ -14,6 +14,10 @@ the minGRU layer": a layer of width 512 applied to a (2, 1024, 512) batch
 returns the same shape; guide "Process a sequence sequentially": per token,
 pass the previous hidden state -- None at first -- with
 return_next_prev_hidden=True and keep the returned state).
+
+mingru_scan is the one convenience beyond the C names: the scan-only
+forward and its backward kernel in a torch.autograd.Function, so that a
+caller can train through the scan (autograd only records the call).
 """
 
 from __future__ import annotations
