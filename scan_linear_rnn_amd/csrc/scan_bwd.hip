@@ -85,7 +85,7 @@ enum Kind { kMinGRU = 0, kMinMax = 1 };
 // step n, are t_n = t_hi - n; loads are clamped into [0, T) and addressed
 // from the lowest row any of them touches, so every buffer offset is
 // non-negative and small.
-template <int KIND, typename TIn, int V, int N, int W, bool kDecay = false>
+template <int KIND, typename TIn, int V, int N, int W, bool kDecay, int SB>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(kBwdWavesPerSimd)))
 void scan_backward_kernel(const BwdParams Q) {
   using R = Raw<TIn, V>;
@@ -225,11 +225,9 @@ void scan_backward_kernel(const BwdParams Q) {
   for (int c = 0; c < V; ++c) s_pre[wave][lane * V + c] = agg[c];
   __syncthreads();
 
-  // Phase 2: the gradient entering the tile (decoupled look-back).
-  // Look-back fallback one word per round trip: wider batches cost this
-  // register-bound kernel more on the common path than they save on long
-  // chains (measured at B=8, T=65536, D=1024: +0.4% for 1, +1.0% for 2).
-  resolve_tile<MinGRUOp, W, Dc, 64 * W, 1>(P, tl, s_pre, s_win, s_hin);
+  // Phase 2: the gradient entering the tile (decoupled look-back), its
+  // fallback walking SB words per round trip (chosen per launch).
+  resolve_tile<MinGRUOp, W, Dc, 64 * W, SB>(P, tl, s_pre, s_win, s_hin);
 
   // Phase 3: replay to get G at every step and form the input gradients.
   float G[V];
@@ -287,13 +285,26 @@ void scan_backward_kernel(const BwdParams Q) {
   }
 }
 
+// Look-back fallback: with many chains a tile's walk is short and one word
+// per round trip costs this register-bound kernel least; with few chains
+// dozens of tiles of a chain are in flight together and walks are long, and
+// four words per round trip pay off.  Measured (bf16, one process): B=8
+// T=65536 D=1024 (64 chains) 1818 / 1826 / 1863 us with 1 / 2 / 4 words;
+// 1 x 65536 x 1024 (8 chains) 314 / 297 / 285 us; 1 x 262144 x 256 (2
+// chains) 644 / 618 / 520 us; at 16 chains all within 1.6%.
+constexpr int64_t kFewChains = 16;
+
 template <int KIND, typename TIn, int V, bool kDecay = false>
 hipError_t launch_bwd_v(const BwdParams& Q, hipStream_t stream) {
   constexpr int N = kBwdElemsPerLane / V;
   static_assert(N + 1 <= 64, "one lane per gap of the run");
   const int64_t n_blocks = Q.core.n_chains * Q.core.n_tchunks;
-  hipLaunchKernelGGL((scan_backward_kernel<KIND, TIn, V, N, kBwdWaves, kDecay>),
-                     dim3(uint32_t(n_blocks)), dim3(64 * kBwdWaves), 0, stream, Q);
+  if (Q.core.n_chains < kFewChains)
+    hipLaunchKernelGGL((scan_backward_kernel<KIND, TIn, V, N, kBwdWaves, kDecay, 4>),
+                       dim3(uint32_t(n_blocks)), dim3(64 * kBwdWaves), 0, stream, Q);
+  else
+    hipLaunchKernelGGL((scan_backward_kernel<KIND, TIn, V, N, kBwdWaves, kDecay, 1>),
+                       dim3(uint32_t(n_blocks)), dim3(64 * kBwdWaves), 0, stream, Q);
   return hipGetLastError();
 }
 
