@@ -234,7 +234,13 @@ struct Narrow {
   static constexpr int kLdB = FULL ? kNarrowCols : kNarrowCols + PAD;
   static constexpr int kLdR = kNarrowCols + PAD;
   static constexpr int kStageFloats = TM * kLdA + kNarrowSK * kLdB;
-  static constexpr int kStagingFloats = kNarrowKG * 2 * kStageFloats;
+  // Full 32-row tiles keep three stages per wave (two in flight while one is
+  // multiplied): a stage holds only 16 MFMAs per wave, too short to cover a
+  // load's latency alone.  64-row tiles keep two (three would not fit).
+  static constexpr int kStages = (FULL && TM == 32) ? 3 : 2;
+  static constexpr int kStageLoads = (TM * kNarrowSK + kNarrowSK * kNarrowCols) / 256;
+  static constexpr int kStagingFloats = kNarrowKG * kStages * kStageFloats;
+  static_assert(kStageLoads * 256 == TM * kNarrowSK + kNarrowSK * kNarrowCols, "whole loads");
   static constexpr int kRedFloats = kNarrowKG * TM * kLdR;  // the waves' sums, over the staging
   static constexpr int kSmemFloats = kStagingFloats > kRedFloats ? kStagingFloats : kRedFloats;
   static_assert(TM == 32 || TM == 64, "tile rows");
@@ -254,6 +260,11 @@ __device__ __forceinline__ void load_lds16(const float* src, float* lds_block) {
 // LDS reads have returned (lgkmcnt), so that the next stage may read the one
 // buffer and overwrite the other.
 __device__ __forceinline__ void wait_stage() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory"); }
+// The same, leaving the last N direct loads (one later stage) in flight.
+template <int N>
+__device__ __forceinline__ void wait_stage_but() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N) : "memory");
+}
 
 __device__ __forceinline__ void put4(float* r, int q, float4 v) {
   r[4 * q] = v.x; r[4 * q + 1] = v.y; r[4 * q + 2] = v.z; r[4 * q + 3] = v.w;
@@ -296,8 +307,8 @@ __global__ __launch_bounds__(64 * kNarrowKG) void narrow_kernel(const GemmParams
   const int64_t kt1 = kt0 + per < n_kt ? kt0 + per : n_kt;
   const int iters = int(per);  // the same for every wave
 
-  // This wave's two stages, kStageFloats apart: A [TM][kLdA], then B [SK][kLdB].
-  float* const stages = smem + g * 2 * G::kStageFloats;
+  // This wave's kStages stages, kStageFloats apart: A [TM][kLdA], then B [SK][kLdB].
+  float* const stages = smem + g * G::kStages * G::kStageFloats;
   auto stage_at = [&](int buf) { return stages + buf * G::kStageFloats; };
   // Offset of A's 4-float chunk (row, k .. k + 3) in a stage (swizzled when full).
   auto a_off = [](int row, int k) {
@@ -439,19 +450,46 @@ __global__ __launch_bounds__(64 * kNarrowKG) void narrow_kernel(const GemmParams
   // Each wave stages and reads only its own buffers, so the K loop needs no
   // workgroup barrier: a wave's LDS accesses take effect in its issue order,
   // and its direct loads are waited for (vmcnt) before it reads them.
-  if constexpr (FULL) {
+  if constexpr (FULL && G::kStages == 3) {
+    // Three stages b0, b1, b2 in rotation; stage it is multiplied from
+    // buffer it % 3 while stages it + 1 and it + 2 load.  One function with
+    // three restrict pointers, so that the compiler sees that reading one
+    // buffer does not wait for the loads into the other two.
+    auto pipeline = [&](float* __restrict__ b0, float* __restrict__ b1, float* __restrict__ b2) {
+      constexpr int L = G::kStageLoads;
+      issue_direct(b0);
+      if (iters > 1) {
+        issue_direct(b1);
+        wait_stage_but<L>();
+      } else {
+        wait_stage();
+      }
+      auto step = [&](const float* __restrict__ cur, float* __restrict__ nxt, int it) {
+        const bool more = it + 2 < iters;
+        if (more) issue_direct(nxt);
+        mfma_stage(cur);
+        if (more) wait_stage_but<L>(); else wait_stage();
+      };
+      for (int it = 0; it < iters; it += 3) {
+        step(b0, b2, it);
+        if (it + 1 < iters) step(b1, b0, it + 1);
+        if (it + 2 < iters) step(b2, b1, it + 2);
+      }
+    };
+    pipeline(stage_at(0), stage_at(1), stage_at(2));
+  } else if constexpr (FULL) {
     issue_direct(stage_at(0));
     wait_stage();
+    for (int it = 0; it < iters; ++it) {
+      const int buf = it & 1;
+      full_stage(stage_at(buf), stage_at(buf ^ 1), it + 1 < iters);
+      wait_stage();
+    }
   } else {
     load_checked(kt0);
     store_stage(stage_at(0));
-  }
-  for (int it = 0; it < iters; ++it) {
-    const int buf = it & 1;
-    if constexpr (FULL) {
-      full_stage(stage_at(buf), stage_at(buf ^ 1), it + 1 < iters);
-      wait_stage();
-    } else {
+    for (int it = 0; it < iters; ++it) {
+      const int buf = it & 1;
       if (it + 1 < iters) load_checked(kt0 + it + 1);
       mfma_stage(stage_at(buf));
       if (it + 1 < iters) store_stage(stage_at(buf ^ 1));
