@@ -28,11 +28,12 @@ with a carried hidden state); the minmaxrnc PyPI page, "The model" item 3 (the
 MinMax update) and "Key properties" (bounded operator, prefix-scan depth);
 the "Your first delta model" tutorial, Step 5 "Adding time decay" (the decay
 contract: a per-event gap decays the carried state at the token boundary).
-The minGRU equations themselves (h_t = (1 - z_t) h_{t-1} + z_t g(p_t),
-z = sigma(k), g(x) = x + 1/2 for x >= 0 else sigma(x), [k, p] = x W_in, the
-identities log(1 - z) = -softplus(k)) are not printed on the pages; they are
-the published minGRU definition (Feng et al., "Were RNNs All We Needed?",
-2024), which the profile's layer implements, written out here as given.
+The pages print no equations for the minGRU layer: the profile names the
+layer, its log-space numerically stable evaluation and its two modes.  The
+recurrence written out here (h_t = (1 - z_t) h_{t-1} + z_t g(p_t), z =
+sigma(k), g(x) = x + 1/2 for x >= 0 else sigma(x), [k, p] = x W_in, with the
+log-space coefficients log(1 - z) = -softplus(k) and log z + log g(p)) is the
+minGRU recurrence those sections refer to, taken as stated.
 
 Parity status of each function is listed in its module docstring.
 """

@@ -1,9 +1,9 @@
 """minGRU layer, run as its plain sequential definition in float64.
 
-The method (the log-space minGRU layer of the minGRU-pytorch profile; the
-equations are the published minGRU definition, Feng et al., "Were RNNs All We
-Needed?", 2024 -- the pages name only the layer, its log-space form and its
-two modes):
+The method (the log-space minGRU layer of the "Mingru Pytorch" profile,
+intro and "Requirements & limits"; the pages name the layer, its log-space
+numerically stable form and its two modes, and print no equations, so the
+minGRU recurrence they refer to is written out as stated):
 
     [k_t | p_t] = x_t W_in            k = first D_h columns, p = the next D_h
     z_t         = sigma(k_t)
