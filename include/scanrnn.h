@@ -13,8 +13,22 @@
  *     h_t = (1 - z_t) h_{t-1} + z_t htilde_t       t = 1..T, h_0 carried (absent = 0)
  *     y_t = h_t W_out                        (absent W_out: y_t = h_t)
  *
- * evaluated with log(1 - z) = -softplus(k) and log z + log g(p) as the
- * coefficients of an associative scan over t.
+ * evaluated as an associative scan over t of the affine maps
+ * h -> a_t h + b_t.  The log-space coefficients log a_t = log(1 - z_t) =
+ * -softplus(k_t) and log b_t = log z_t + log g(p_t) are exponentiated in
+ * closed form (a_t = sigma(-k_t), b_t = sigma(k_t) g(p_t), no cancelling
+ * 1 - x), and composed maps carry their coefficient A together with its
+ * complement 1 - A, so that a long memory (A near 1) keeps 1 - A to a few
+ * ulps -- what the log-space form's -softplus(k) keeps -- while the state
+ * itself stays linear (a signed h_0 needs no logarithm).  The single-token
+ * step evaluates h_{t-1} + z_t (g(p_t) - h_{t-1}).
+ *
+ * Range.  For |k| above about 87.3 the smaller of sigma(k) and sigma(-k) is
+ * below the smallest normal fp32 number and flushes to zero, and the term it
+ * multiplies (the candidate's share for very negative k, the carried state
+ * for very positive k) is dropped; every other term keeps full accuracy.
+ * The scans report such gate logits through scanrnn_workspace_status
+ * (SR_ERR_GATE_RANGE); the results are still written.
  *
  * MinMax neuron (minmaxrnc PyPI page, "The model" item 3):
  *
@@ -62,7 +76,8 @@ typedef enum {
   SR_ERR_UNSUPPORTED = 2,        /* valid request the library does not handle   */
   SR_ERR_WORKSPACE_TOO_SMALL = 3,
   SR_ERR_HIP = 4,                /* a HIP runtime call failed                   */
-  SR_ERR_LOOKBACK_TIMEOUT = 5    /* reported by scanrnn_workspace_status only   */
+  SR_ERR_LOOKBACK_TIMEOUT = 5,   /* reported by scanrnn_workspace_status only   */
+  SR_ERR_GATE_RANGE = 6          /* reported by scanrnn_workspace_status only   */
 } sr_status;
 
 typedef enum { SR_F32 = 0, SR_BF16 = 1 } sr_dtype;
@@ -265,9 +280,12 @@ const char* scanrnn_last_error(void);
  * Pass SCANRNN_LOOKBACK_SPIN_LIMIT to restore the default. */
 sr_status scanrnn_set_lookback_spin_limit(uint32_t polls);
 
-/* Waits for `stream`, then reports whether a scan that used `workspace` since
- * its last reset gave up waiting for a predecessor chunk (a bounded wait that
- * should never expire; SR_ERR_LOOKBACK_TIMEOUT if it did, SR_OK otherwise). */
+/* Waits for `stream`, then reports what the scans that used `workspace` since
+ * its last reset met: SR_ERR_LOOKBACK_TIMEOUT if one gave up waiting for a
+ * predecessor chunk (a bounded wait that should never expire), else
+ * SR_ERR_GATE_RANGE if a minGRU scan (forward, fused forward) met a gate
+ * logit beyond the fp32 range of sigma (|k| above about 87.3; see the range
+ * note at the top), else SR_OK. */
 sr_status scanrnn_workspace_status(const void* workspace, void* stream);
 
 /* Library version, "major.minor.patch". */

@@ -51,6 +51,7 @@ SR_ERR_UNSUPPORTED = 2
 SR_ERR_WORKSPACE_TOO_SMALL = 3
 SR_ERR_HIP = 4
 SR_ERR_LOOKBACK_TIMEOUT = 5
+SR_ERR_GATE_RANGE = 6
 SR_F32 = 0
 SR_BF16 = 1
 LOOKBACK_SPIN_LIMIT = 1 << 20  # SCANRNN_LOOKBACK_SPIN_LIMIT

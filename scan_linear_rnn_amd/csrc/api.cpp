@@ -516,7 +516,9 @@ sr_status scanrnn_workspace_status(const void* workspace, void* stream) {
                                   hipMemcpyDeviceToHost, s);
   if (err == hipSuccess) err = hipStreamSynchronize(s);
   if (err != hipSuccess) return fail(SR_ERR_HIP, "reading workspace status: %s", hipGetErrorString(err));
-  if (flag != 0) return fail(SR_ERR_LOOKBACK_TIMEOUT, "a scan gave up waiting for a predecessor tile");
+  if (flag & 1u) return fail(SR_ERR_LOOKBACK_TIMEOUT, "a scan gave up waiting for a predecessor tile");
+  if (flag & 2u)
+    return fail(SR_ERR_GATE_RANGE, "a gate logit beyond the fp32 range of sigma (|k| > ~87.3) was met");
   return SR_OK;
 }
 

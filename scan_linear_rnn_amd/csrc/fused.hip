@@ -53,7 +53,7 @@ void fused_proj_scan_kernel(const FusedParams F) {
   __shared__ float As[2][BK][kTileT + PAD];
   __shared__ float Bs[2][BK][BN + PAD];
   __shared__ uint32_t s_ticket;
-  __shared__ Pair s_pre[kTileT / 64][kTileD];
+  __shared__ Affine s_pre[kTileT / 64][kTileD];
   __shared__ uint64_t s_win[kWindowTiles][kTileD];
   __shared__ float s_hin[kTileD];
   __shared__ float s_gap[kTileT];
@@ -87,51 +87,55 @@ void fused_proj_scan_kernel(const FusedParams F) {
   tile_mainloop<kStep, kTileT, kFull>(F.g, tl.b * P.T + t0, rows, tl.d0, 0, F.g.K, As, Bs, acc);
 
   // 1. Maps in place of the sums (set 0 <- coefficient, set 1 <- offset);
-  // rows past T become the identity.  Then the runs of 4 rows: run n = (i, q),
-  // n = 4*i + q.
+  // rows past T become the identity.  Each run of 4 rows (run n = (i, q),
+  // n = 4*i + q) is composed as its maps are formed, with the complements
+  // (see Affine), which are not kept per row.
   bool sat = false;
+  uint32_t gate_lo = 0x3F800000u;  // bits of 1.0f
+  Affine mine[8];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int n = 0; n < 8; ++n) {
+    const int i = n / 4, q = n % 4;
+    Affine run_n = MinGRUOp::identity();
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int lr = wm * 64 + i * 32 + (r / 4) * 8 + kl * 4 + (r % 4);
-      Pair m = MinGRUOp::element(acc[i][0][r], acc[i][1][r]);
+    for (int j = 0; j < 4; ++j) {
+      const int r = 4 * q + j;
+      const int lr = wm * 64 + i * 32 + q * 8 + kl * 4 + j;
+      Affine m = MinGRUOp::element(acc[i][0][r], acc[i][1][r]);
+      if (lr < rows) gate_lo = MinGRUOp::gate_floor(m, gate_lo);
       if constexpr (kDecay) {
         const float gp = s_gap[lr];
-        m.u *= __builtin_amdgcn_exp2f(nrate * gp);
+        float gamma, om;
+        decay_factors(nrate * gp, gamma, om);
+        m = MinGRUOp::decayed(m, gamma, om);
         sat = sat || (rate * gp > kDecayClamp);
       }
       if (lr >= rows) m = MinGRUOp::identity();
-      acc[i][0][r] = m.u;
-      acc[i][1][r] = m.v;
+      acc[i][0][r] = m.a;
+      acc[i][1][r] = m.b;
+      run_n = MinGRUOp::push(run_n, m);
     }
+    mine[n] = run_n;
   }
   if constexpr (kDecay) {
     if (P.saturated != nullptr && __builtin_amdgcn_ballot_w64(sat) != 0 && lane == 0)
       __hip_atomic_fetch_or(P.saturated, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  Pair mine[8];
-#pragma unroll
-  for (int n = 0; n < 8; ++n) {
-    const int i = n / 4, q = n % 4;
-    Pair m = {acc[i][0][4 * q], acc[i][1][4 * q]};
-#pragma unroll
-    for (int j = 1; j < 4; ++j)
-      m = MinGRUOp::compose(m, Pair{acc[i][0][4 * q + j], acc[i][1][4 * q + j]});
-    mine[n] = m;
-  }
+  if (__builtin_amdgcn_ballot_w64(gate_lo < kMinNormalBits && chan_ok) != 0 && lane == 0)
+    __hip_atomic_fetch_or(P.status, kStatusGateRange, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   // 2. The partner lane's runs (lane ^ 32), then the prefix over the wave's
   // 16 runs in T order: run 2n is lane kl = 0's run n, run 2n + 1 lane 1's.
   Pair pre[8];
-  Pair run = MinGRUOp::identity();
+  Affine run = MinGRUOp::identity();
 #pragma unroll
   for (int n = 0; n < 8; ++n) {
-    const Pair other = {__shfl_xor(mine[n].u, 32), __shfl_xor(mine[n].v, 32)};
-    const Pair even = kl == 0 ? mine[n] : other;
-    const Pair odd = kl == 0 ? other : mine[n];
-    if (kl == 0) pre[n] = run;
+    const Affine other = {__shfl_xor(mine[n].a, 32), __shfl_xor(mine[n].c, 32),
+                          __shfl_xor(mine[n].b, 32)};
+    const Affine even = kl == 0 ? mine[n] : other;
+    const Affine odd = kl == 0 ? other : mine[n];
+    if (kl == 0) pre[n] = MinGRUOp::map(run);
     run = MinGRUOp::compose(run, even);
-    if (kl == 1) pre[n] = run;
+    if (kl == 1) pre[n] = MinGRUOp::map(run);
     run = MinGRUOp::compose(run, odd);
   }
   // 3. Wave rows along T, then the look-back across tiles.
@@ -140,7 +144,7 @@ void fused_proj_scan_kernel(const FusedParams F) {
   resolve_tile<MinGRUOp, kTileT / 64, kTileD, 2 * kTileT, 2>(P, tl, s_pre, s_win, s_hin);
 
   // 4. Replay and store.
-  const float h_wave = MinGRUOp::apply(s_pre[wm][c], s_hin[c]);
+  const float h_wave = MinGRUOp::apply(MinGRUOp::map(s_pre[wm][c]), s_hin[c]);
   float* out = P.out + (tl.b * P.T + t0) * P.D + d;
 #pragma unroll
   for (int n = 0; n < 8; ++n) {

@@ -6,7 +6,7 @@
 // Step mode (the single-token step of the minGRU profile's sequential guide):
 // with paired k / p columns one lane holds k and p of the same (row, d), and
 // the epilogue computes
-//     z = sigma(k), a = 1 - z = sigma(-k), h_next = a h_prev + z g(p)
+//     z = sigma(k), h_next = (1 - z) h_prev + z g(p) = h_prev + z (g(p) - h_prev)
 // without writing [k | p] anywhere.
 
 #include "gemm_tile.hpp"
@@ -16,13 +16,12 @@ namespace {
 
 using namespace gt;
 
-__device__ __forceinline__ float sigmoid_pos_neg(float k, float& one_minus) {
+// sigma(k) from e = e^{-|k|}: 1/(1+e) for k >= 0, e/(1+e) below.
+__device__ __forceinline__ float sigmoid_f(float k) {
   constexpr float kLog2e = 1.4426950408889634f;
   const float e = __builtin_amdgcn_exp2f(-fabsf(k) * kLog2e);
   const float big = __builtin_amdgcn_rcpf(1.0f + e);
-  const float small = e * big;
-  one_minus = k >= 0.0f ? small : big;
-  return k >= 0.0f ? big : small;
+  return k >= 0.0f ? big : e * big;
 }
 
 __device__ __forceinline__ float g_act(float p) {
@@ -48,11 +47,13 @@ __device__ __forceinline__ float carried_state(const GemmParams& P, int64_t row,
   return hp;
 }
 
-// h_next = (1 - z) h + z g(p) with z = sigma(k), h the carried state.
+// h_next = (1 - z) h + z g(p) with z = sigma(k), h the carried state,
+// evaluated as the interpolation h + z (g(p) - h): the complement 1 - z is
+// never rounded on its own, so a gate that keeps almost all of the state
+// (z tiny) moves it by exactly z times the gap to the candidate, and h = g(p)
+// is a fixed point.
 __device__ __forceinline__ float step_value(float k, float p, float h) {
-  float a;
-  const float z = sigmoid_pos_neg(k, a);
-  return fmaf(a, h, z * g_act(p));
+  return fmaf(sigmoid_f(k), g_act(p) - h, h);
 }
 
 __device__ __forceinline__ void step_update(const GemmParams& P, int64_t row, int64_t d, float k,

@@ -88,8 +88,9 @@ void chunk_scan_kernel(const ScanParams P) {
   constexpr int N = kElemsPerLane / V;
   constexpr int W = kWaves;
   using R = Raw<TIn, V>;
+  using Agg = typename Op::Agg;
   __shared__ uint32_t s_ticket;
-  __shared__ Pair s_pre[W][64 * V];
+  __shared__ Agg s_pre[W][64 * V];
   __shared__ uint64_t s_win[kWindowTiles][64 * V];
   __shared__ float s_hin[64 * V];
 
@@ -103,23 +104,29 @@ void chunk_scan_kernel(const ScanParams P) {
   const uint32_t chain = ticket % n_chains;
   const int64_t tchunk = ticket / n_chains;
   const int64_t b = chain / n_dtiles;
-  const int64_t d = int64_t(chain % n_dtiles) * (64 * V) + lane * V;
+  const int64_t dtile_first = int64_t(chain % n_dtiles) * (64 * V);
+  const int64_t d = dtile_first + lane * V;
   const bool lane_on = d < P.D;
   const int64_t tw = tchunk * (W * N) + wave * N;  // first step of this wave's run
+  // The run's rows and the lane's channel, clamped so that every load stays
+  // inside the tensor (scan_addr.hpp); steps [0, nvalid) of the run lie
+  // inside the sequence (wave-uniform).
+  addr::FwdRun run = addr::fwd_run(P.T, P.D, V, N, tw, dtile_first, lane);
+  // The row clamps depend on the wave only: said so, they stay in scalar
+  // registers (a per-lane row offset would need a loop per buffer load).
+  run.nvalid = __builtin_amdgcn_readfirstlane(run.nvalid);
+  run.n_last = __builtin_amdgcn_readfirstlane(run.n_last);
+  const int nvalid = run.nvalid;
+  const int64_t t_base = run.t_base;
 
-  // Phase 1: load, transform, compose.  Loads need no branches: past the
-  // end of the tensor they return zero, and every map outside [0,T) x [0,D)
-  // is replaced by the identity.
-  // The wave's rows start at (b, tw); row n of the run is n*ld elements on.
+  // Phase 1: load, transform, compose.
   const int64_t esz = sizeof(TIn);
-  const int64_t row0 = b * P.T + tw;
-  const int64_t dtile_first = int64_t(chain % n_dtiles) * (64 * V);
-  const int64_t base_el = row0 * P.ld_in + dtile_first;
+  const int64_t base_el = (b * P.T + t_base) * P.ld_in + dtile_first;
   const int64_t end_el = (P.B * P.T - 1) * P.ld_in + P.D;  // one past the last element
   const rsrc_t r0 = make_rsrc(static_cast<const TIn*>(P.in0) + base_el, (end_el - base_el) * esz);
   const rsrc_t r1 = make_rsrc(static_cast<const TIn*>(P.in1) + base_el, (end_el - base_el) * esz);
-  const int voff_in = int(lane * V * esz);
-  const int row_bytes = int(P.ld_in * esz);
+  const int voff_in = int(run.lane_ch * esz);
+  const int row_bytes = int(P.ld_in * esz);  // N * row_bytes < 2^31: checked on the host
   // Time decay: -rate * log2(e) for each of the lane's channels, and the gap
   // of step n of the run held by lane n (one load per wave; the step's gap
   // is then read from that lane, so it is uniform across the wave).  Rates
@@ -130,9 +137,10 @@ void chunk_scan_kernel(const ScanParams P) {
   typename Raw<float, V>::type rate_raw{};
   if constexpr (kDecay) {
     // Buffer loads throughout: channels past D, lanes >= N and steps past T
-    // fall outside the descriptors' extents and read zero, with no branch
-    // (a branch around a load would make the wave wait for it right there).
-    const int64_t n_gaps = P.T - tw < N ? (P.T - tw > 0 ? P.T - tw : 0) : N;
+    // fall outside the descriptors' extents (per-lane offsets, soffset 0)
+    // and read zero, with no branch (a branch around a load would make the
+    // wave wait for it right there).
+    const int64_t n_gaps = nvalid;
     const rsrc_t rg = make_rsrc(P.gap + (tw < P.T ? b * P.T + tw : 0), n_gaps * 4);
     gap_l = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, lane * 4, 0, 0));
     const rsrc_t rr = make_rsrc(P.rate + dtile_first, (P.D - dtile_first) * 4);
@@ -141,8 +149,9 @@ void chunk_scan_kernel(const ScanParams P) {
   typename R::type raw0[N], raw1[N];
 #pragma unroll
   for (int n = 0; n < N; ++n) {
-    raw0[n] = R::load(r0, voff_in, n * row_bytes);
-    raw1[n] = R::load(r1, voff_in, n * row_bytes);
+    const int soff = addr::fwd_row(run, n) * row_bytes;  // scalar
+    raw0[n] = R::load(r0, voff_in, soff);
+    raw1[n] = R::load(r1, voff_in, soff);
   }
   if constexpr (kDecay) {
     if (P.log1p_gap) gap_l = log1pf(gap_l);  // after the input loads are issued
@@ -151,30 +160,38 @@ void chunk_scan_kernel(const ScanParams P) {
     for (int c = 0; c < V; ++c) nrate[c] *= kNegLog2e;
   }
   Pair e[N][V];
-  Pair agg[V];
+  Agg agg[V];
 #pragma unroll
   for (int c = 0; c < V; ++c) agg[c] = Op::identity();
-  // Steps [0, nvalid) of the run lie inside the sequence (a wave-uniform
-  // bound, so the test is a scalar branch); lanes past D are reset below.
-  // Out-of-range maps are still replayed in phase 3 but never stored.
-  const int64_t rem = P.T - tw;
-  const int nvalid = rem <= 0 ? 0 : (rem >= N ? N : int(rem));
+  uint32_t gate_lo = 0x3F800000u;  // bits of 1.0f
 #pragma unroll
   for (int n = 0; n < N; ++n) {
     float x0[V], x1[V];
     R::unpack(raw0[n], x0);
     R::unpack(raw1[n], x1);
+    typename Op::Step st[V], raw_st[V];
 #pragma unroll
-    for (int c = 0; c < V; ++c) e[n][c] = Op::element(x0[c], x1[c]);
+    for (int c = 0; c < V; ++c) st[c] = raw_st[c] = Op::element(x0[c], x1[c]);
     if constexpr (kDecay) {
       const float gn = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gap_l), n));
       gap_max = fmaxf(gap_max, gn);
 #pragma unroll
-      for (int c = 0; c < V; ++c) e[n][c].u *= __builtin_amdgcn_exp2f(nrate[c] * gn);
+      for (int c = 0; c < V; ++c) {
+        float gamma, om;
+        decay_factors(nrate[c] * gn, gamma, om);
+        st[c] = Op::decayed(st[c], gamma, om);
+      }
     }
+#pragma unroll
+    for (int c = 0; c < V; ++c) e[n][c] = Op::step_map(st[c]);
+    // Steps inside the sequence join the run's map and the gate check (one
+    // wave-uniform test per step).
     if (n < nvalid) {
 #pragma unroll
-      for (int c = 0; c < V; ++c) agg[c] = Op::compose(agg[c], e[n][c]);
+      for (int c = 0; c < V; ++c) {
+        agg[c] = Op::push(agg[c], st[c]);
+        gate_lo = Op::gate_floor(raw_st[c], gate_lo);
+      }
     }
     // Keep the scheduler from interleaving many steps' temporaries while
     // all of the run's loads are still holding their registers.
@@ -183,6 +200,12 @@ void chunk_scan_kernel(const ScanParams P) {
   if (!lane_on) {
 #pragma unroll
     for (int c = 0; c < V; ++c) agg[c] = Op::identity();
+  }
+  // Flags: a gate logit beyond the fp32 range of sigma (valid steps and
+  // channels only), and time-decay saturation.
+  if constexpr (Op::kHasGateRange) {
+    if (__builtin_amdgcn_ballot_w64(gate_lo < kMinNormalBits && lane_on) != 0 && lane == 0)
+      __hip_atomic_fetch_or(P.status, kStatusGateRange, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   if constexpr (kDecay) {
     if (P.saturated != nullptr) {
@@ -198,27 +221,30 @@ void chunk_scan_kernel(const ScanParams P) {
   __syncthreads();
 
   // Phase 2: the state entering the tile (decoupled look-back).
-  resolve_tile<Op, W, 64 * V>(P, Tile{tchunk, b, int64_t(chain % n_dtiles) * (64 * V)}, s_pre,
-                              s_win, s_hin);
+  resolve_tile<Op, W, 64 * V>(P, Tile{tchunk, b, dtile_first}, s_pre, s_win, s_hin);
 
-  // Phase 3: replay the maps from the state entering this wave's run.
-  float h[V];
+  // Phase 3: replay the maps from the state entering this wave's run and
+  // store the valid steps (a scalar bound; lanes past D store nothing).
+  if (lane_on) {
+    float h[V];
 #pragma unroll
-  for (int c = 0; c < V; ++c) h[c] = Op::apply(s_pre[wave][lane * V + c], s_hin[lane * V + c]);
-  const int64_t out_base = row0 * P.D + dtile_first;
-  const rsrc_t ro = make_rsrc(P.out + out_base, (P.B * P.T * P.D - out_base) * 4);
-  const int voff_out = lane * V * 4;
-  const int out_row_bytes = int(P.D * 4);
+    for (int c = 0; c < V; ++c)
+      h[c] = Op::apply(Op::map(s_pre[wave][lane * V + c]), s_hin[lane * V + c]);
+    const int64_t out_base = (b * P.T + t_base) * P.D + dtile_first;
+    const rsrc_t ro = make_rsrc(P.out + out_base, (P.B * P.T * P.D - out_base) * 4);
+    const int voff_out = lane * V * 4;
+    const int out_row_bytes = int(P.D * 4);  // N * out_row_bytes < 2^31: checked on the host
+    const int64_t n_final = P.T - 1 - tw;   // the step holding h_T, if in this run
 #pragma unroll
-  for (int n = 0; n < N; ++n) {
+    for (int n = 0; n < N; ++n) {
 #pragma unroll
-    for (int c = 0; c < V; ++c) h[c] = Op::apply(e[n][c], h[c]);
-    const int64_t t = tw + n;
-    if (lane_on && t < P.T) {
-      OutVec<V>::store(ro, voff_out, n * out_row_bytes, h);
-      if (P.last != nullptr && t == P.T - 1) {
+      for (int c = 0; c < V; ++c) h[c] = Op::apply(e[n][c], h[c]);
+      if (n < nvalid) {
+        OutVec<V>::store(ro, voff_out, n * out_row_bytes, h);
+        if (P.last != nullptr && n == n_final) {
 #pragma unroll
-        for (int c = 0; c < V; ++c) P.last[size_t(b) * P.D + d + c] = h[c];
+          for (int c = 0; c < V; ++c) P.last[size_t(b) * P.D + d + c] = h[c];
+        }
       }
     }
   }
@@ -349,6 +375,12 @@ sr_status launch_scan(const ScanRequest& rq) {
   if (P.n_chains * P.n_tchunks * (64 * kWaves) > int64_t(0xFFFFFFFFu))
     return fail(SR_ERR_UNSUPPORTED, "scan of %lld tiles exceeds one launch's grid",
                 (long long)(P.n_chains * P.n_tchunks));
+  // A wave addresses its rows with 32-bit scalar offsets of up to N rows.
+  const int64_t esz = rq.in_dtype == SR_BF16 ? 2 : 4;
+  const int64_t max_row_bytes = rq.ld_in * esz > rq.D * 4 ? rq.ld_in * esz : rq.D * 4;
+  if (max_row_bytes * g.N > int64_t(0x7FFFFFFF))
+    return fail(SR_ERR_UNSUPPORTED, "scan rows of %lld bytes are too long",
+                (long long)max_row_bytes);
   if (rq.check_only) return SR_OK;
   char* ws = static_cast<char*>(rq.workspace);
   P.counter = reinterpret_cast<uint32_t*>(ws);

@@ -36,8 +36,8 @@ namespace sr {
 namespace {
 using namespace eng;
 
-constexpr int kBwdWaves = 8;
-constexpr int kBwdElemsPerLane = 16;  // N * V steps kept per lane
+constexpr int kBwdWaves = addr::kBwdWaves;
+constexpr int kBwdElemsPerLane = addr::kBwdElemsPerLane;  // N * V steps kept per lane
 constexpr int kBwdWavesPerSimd = 4;
 
 struct BwdParams {
@@ -93,7 +93,7 @@ void scan_backward_kernel(const BwdParams Q) {
   constexpr int Dc = 64 * V;
   const ScanParams& P = Q.core;
   __shared__ uint32_t s_ticket;
-  __shared__ Pair s_pre[W][Dc];
+  __shared__ Affine s_pre[W][Dc];
   __shared__ uint64_t s_win[kWindowTiles][Dc];
   __shared__ float s_hin[Dc];
 
@@ -104,14 +104,23 @@ void scan_backward_kernel(const BwdParams Q) {
   const int64_t d = tl.d0 + lane * V;
   const bool lane_on = d < P.D;
   const int64_t T = P.T;
-  const int64_t t_hi = T - 1 - (tl.tchunk * (W * N) + int64_t(wave) * N);
-  const int nvalid = t_hi < 0 ? 0 : (t_hi + 1 >= N ? N : int(t_hi + 1));
-  const int64_t rbase = t_hi - N > 0 ? t_hi - N : 0;
+  // The run's rows (clamped into [0, T), addressed from the lowest one) and
+  // the lane's channel, so that every access stays inside its tensor
+  // (scan_addr.hpp).
+  addr::BwdRun run = addr::bwd_run(T, P.D, V, N, tl.tchunk, wave, W, tl.d0, lane);
+  // The row offsets depend on the wave only: said so, they stay in scalar
+  // registers (a per-lane row offset would need a loop per buffer access).
+  run.nvalid = __builtin_amdgcn_readfirstlane(run.nvalid);
+  run.rbase = (int64_t(__builtin_amdgcn_readfirstlane(int(run.rbase >> 32))) << 32) |
+              uint32_t(__builtin_amdgcn_readfirstlane(int(run.rbase)));
+  run.t_hi = (int64_t(__builtin_amdgcn_readfirstlane(int(run.t_hi >> 32))) << 32) |
+             uint32_t(__builtin_amdgcn_readfirstlane(int(run.t_hi)));
+  const int64_t t_hi = run.t_hi;
+  const int nvalid = run.nvalid;
   auto soff = [&](int64_t row, int64_t row_bytes) -> int {
-    const int64_t r = row < 0 ? 0 : (row > T - 1 ? T - 1 : row);
-    return int((r - rbase) * row_bytes);
+    return int(addr::bwd_row(run, T, row) * row_bytes);
   };
-  const int64_t row0 = tl.b * T + rbase;
+  const int64_t row0 = tl.b * T + run.rbase;
 
   // Descriptors over the inputs, the forward states and the gradients.
   const int64_t esz = sizeof(TIn);
@@ -123,7 +132,7 @@ void scan_backward_kernel(const BwdParams Q) {
   const int64_t f_end = P.B * T * P.D;
   const rsrc_t rf = make_rsrc(Q.fwd + f_base, (f_end - f_base) * 4);
   const rsrc_t rg = make_rsrc(Q.grad + f_base, (f_end - f_base) * 4);
-  const int vin = int(lane * V * esz), vf = lane * V * 4;
+  const int vin = int(run.lane_ch * esz), vf = int(run.lane_ch * 4);
   const int64_t in_row = Q.ld_in * esz, f_row = P.D * 4;
 
   // Time decay: -rate * log2(e) for the lane's channels, and lane i holding
@@ -163,14 +172,18 @@ void scan_backward_kernel(const BwdParams Q) {
     for (int c = 0; c < V; ++c) nrate[c] = rv[c] * kNegLog2e;
     if (Q.log1p_gap) gap_l = log1pf(gap_l);  // after the input loads are issued
   }
-  // The decay factor of step (t_hi + 1 - i) for each of the lane's channels.
-  auto decay_at = [&](int i, float (&gam)[V]) {
+  // The decay factor of step (t_hi + 1 - i) for each of the lane's channels,
+  // and its complement 1 - gamma.
+  auto decay_at = [&](int i, float (&gam)[V], float (&om)[V]) {
 #pragma unroll
-    for (int c = 0; c < V; ++c) gam[c] = 1.0f;
+    for (int c = 0; c < V; ++c) {
+      gam[c] = 1.0f;
+      om[c] = 0.0f;
+    }
     if constexpr (kDecay) {
       const float gp = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gap_l), i));
 #pragma unroll
-      for (int c = 0; c < V; ++c) gam[c] = __builtin_amdgcn_exp2f(nrate[c] * gp);
+      for (int c = 0; c < V; ++c) decay_factors(nrate[c] * gp, gam[c], om[c]);
     }
   };
 
@@ -180,26 +193,21 @@ void scan_backward_kernel(const BwdParams Q) {
   for (int c = 0; c < V; ++c)
     init_state[c] = (lane_on && Q.fwd0 != nullptr) ? Q.fwd0[size_t(tl.b) * P.D + d + c] : 0.0f;
 
-  // Phase 1: the maps G -> coef G + grad of the run's steps, composed.
-  Pair e[N][V];
-  Pair agg[V];
-#pragma unroll
-  for (int c = 0; c < V; ++c) agg[c] = MinGRUOp::identity();
-#pragma unroll
-  for (int n = 0; n < N; ++n) {
-    const int64_t t = t_hi - n;
-    float gv[V];
-    RF::unpack(gr[n], gv);
-    float coef[V];
+  // The coefficient of the map of step n of the run (time t = t_hi - n):
+  // that of the following step, a_{t+1} gamma_{t+1} (minGRU) or whether the
+  // state passes step t+1 (MinMax), with its complement; 1 (complement 0)
+  // for t = T - 1, where the gradient on the returned final state enters.
+  auto step_coef = [&](int n, float (&coef)[V], float (&comp)[V]) {
     if (KIND == kMinGRU) {
-      float kn[V], gam[V];
+      float kn[V], gam[V], om[V];
       R::unpack(i0[n], kn);  // k_{t+1}
-      decay_at(n, gam);      // gamma_{t+1}
+      decay_at(n, gam, om);  // gamma_{t+1}
 #pragma unroll
       for (int c = 0; c < V; ++c) {
         float z, a;
         sig_pair(kn[c], z, a);
         coef[c] = a * gam[c];
+        comp[c] = fmaf(a, om[c], z);  // 1 - a gamma = z + a (1 - gamma)
       }
     } else {
       float rn[V], sn[V], xn[V];
@@ -207,13 +215,35 @@ void scan_backward_kernel(const BwdParams Q) {
       R::unpack(i1[n], sn);   // s_{t+1}
       RF::unpack(fw[n], xn);  // x_{t+1}
 #pragma unroll
-      for (int c = 0; c < V; ++c) coef[c] = selection(rn[c], sn[c], xn[c]) == 0 ? 1.0f : 0.0f;
+      for (int c = 0; c < V; ++c) {
+        coef[c] = selection(rn[c], sn[c], xn[c]) == 0 ? 1.0f : 0.0f;
+        comp[c] = 1.0f - coef[c];
+      }
     }
+    if (t_hi - n == T - 1) {
 #pragma unroll
-    for (int c = 0; c < V; ++c) e[n][c] = Pair{t == T - 1 ? 1.0f : coef[c], gv[c]};
+      for (int c = 0; c < V; ++c) {
+        coef[c] = 1.0f;
+        comp[c] = 0.0f;
+      }
+    }
+  };
+
+  // Phase 1: the maps G -> coef G + grad of the run's steps, composed with
+  // their complements 1 - coef (see Affine).  The maps are not kept: phase 3
+  // gets each step's coefficient as the one it forms for the step before
+  // (bit for bit the same arithmetic), and the gradient is still loaded.
+  Affine agg[V];
+#pragma unroll
+  for (int c = 0; c < V; ++c) agg[c] = MinGRUOp::identity();
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    float gv[V], coef[V], comp[V];
+    RF::unpack(gr[n], gv);
+    step_coef(n, coef, comp);
     if (n < nvalid) {
 #pragma unroll
-      for (int c = 0; c < V; ++c) agg[c] = MinGRUOp::compose(agg[c], e[n][c]);
+      for (int c = 0; c < V; ++c) agg[c] = MinGRUOp::push(agg[c], Affine{coef[c], comp[c], gv[c]});
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -230,30 +260,42 @@ void scan_backward_kernel(const BwdParams Q) {
   resolve_tile<MinGRUOp, W, Dc, 64 * W, SB>(P, tl, s_pre, s_win, s_hin);
 
   // Phase 3: replay to get G at every step and form the input gradients.
-  float G[V];
+  // coef_next: the coefficient of the next step's map (the first from the
+  // step after the run, then each step's own pass_or_a).
+  float G[V], coef_next[V];
 #pragma unroll
   for (int c = 0; c < V; ++c)
-    G[c] = MinGRUOp::apply(s_pre[wave][lane * V + c], s_hin[lane * V + c]);
+    G[c] = MinGRUOp::apply(MinGRUOp::map(s_pre[wave][lane * V + c]), s_hin[lane * V + c]);
+  {
+    float comp0[V];
+    step_coef(0, coef_next, comp0);
+  }
   const rsrc_t o0 = make_rsrc(Q.d0 + f_base, (f_end - f_base) * 4);
   const rsrc_t o1 = make_rsrc(Q.d1 + f_base, (f_end - f_base) * 4);
+  uint32_t gate_lo = 0x3F800000u;  // smallest sigma(+-k_t) of the valid steps (bits)
 #pragma unroll
   for (int n = 0; n < N; ++n) {
     const int64_t t = t_hi - n;
+    {
+      float gv[V];
+      RF::unpack(gr[n], gv);
 #pragma unroll
-    for (int c = 0; c < V; ++c) G[c] = MinGRUOp::apply(e[n][c], G[c]);
+      for (int c = 0; c < V; ++c) G[c] = MinGRUOp::apply(Pair{coef_next[c], gv[c]}, G[c]);
+    }
     float o0v[V], o1v[V], pass_or_a[V];
     if (KIND == kMinGRU) {
-      float kt[V], pt[V], hp[V], gam[V];
+      float kt[V], pt[V], hp[V], gam[V], om[V];
       R::unpack(i0[n + 1], kt);
       R::unpack(i1[n], pt);
       RF::unpack(fw[n], hp);
-      decay_at(n + 1, gam);  // gamma_t
+      decay_at(n + 1, gam, om);  // gamma_t
 #pragma unroll
       for (int c = 0; c < V; ++c) {
         const float h_prev = (t == 0 ? init_state[c] : hp[c]) * gam[c];
         float z, a, g, gs;
         sig_pair(kt[c], z, a);
         g_and_slope(pt[c], g, gs);
+        if (n < nvalid) gate_lo = MinGRUOp::gate_floor(Affine{a, z, 0.0f}, gate_lo);
         // z a first, then the difference, then G: z a can sit at the bottom
         // of the normal range (|k| near 87), and G z a would go subnormal.
         o0v[c] = ((z * a) * (g - h_prev)) * G[c];
@@ -274,6 +316,8 @@ void scan_backward_kernel(const BwdParams Q) {
         pass_or_a[c] = sel == 0 ? 1.0f : 0.0f;
       }
     }
+#pragma unroll
+    for (int c = 0; c < V; ++c) coef_next[c] = pass_or_a[c];
     if (lane_on && n < nvalid) {
       OutVec<V>::store(o0, vf, soff(t, f_row), o0v);
       OutVec<V>::store(o1, vf, soff(t, f_row), o1v);
@@ -282,6 +326,10 @@ void scan_backward_kernel(const BwdParams Q) {
         for (int c = 0; c < V; ++c) Q.dinit[size_t(tl.b) * P.D + d + c] = pass_or_a[c] * G[c];
       }
     }
+  }
+  if (KIND == kMinGRU) {
+    if (__builtin_amdgcn_ballot_w64(gate_lo < kMinNormalBits && lane_on) != 0 && lane == 0)
+      __hip_atomic_fetch_or(P.status, kStatusGateRange, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 

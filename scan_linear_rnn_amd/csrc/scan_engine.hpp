@@ -5,6 +5,7 @@
 #pragma once
 
 #include "internal.hpp"
+#include "scan_addr.hpp"
 
 namespace sr {
 namespace eng {
@@ -14,8 +15,14 @@ constexpr uint32_t kTagEmpty = 0xFFFFFFFFu;
 constexpr uint32_t kTagState = 0xFFFFFFFEu;
 constexpr uint32_t kCanonNaN = 0x7FC00000u;
 constexpr size_t kHeaderBytes = 256;
-constexpr int kWaves = 12;           // waves per workgroup
-constexpr int kElemsPerLane = 24;    // N * V: maps each lane keeps in registers
+// Bit pattern of the smallest normal fp32 number: a non-negative gate factor
+// whose bits are below it has flushed.
+constexpr uint32_t kMinNormalBits = 0x00800000u;
+// Bits of the workspace status word (header word 1).
+constexpr uint32_t kStatusTimeout = 1u;    // a look-back wait gave up
+constexpr uint32_t kStatusGateRange = 2u;  // a gate logit beyond the fp32 range of sigma
+constexpr int kWaves = addr::kFwdWaves;               // waves per workgroup
+constexpr int kElemsPerLane = addr::kFwdElemsPerLane; // N * V: maps each lane keeps in registers
 constexpr int kWavesPerSimd = 6;     // register budget: waves resident per SIMD
 constexpr int kWindowTiles = 4;      // most preceding tiles whose look-back words one round trip fetches
 
@@ -23,40 +30,110 @@ struct Pair {
   float u, v;
 };
 
+// An affine map h -> a h + b carried with its complement c = 1 - a.  Both a
+// and c are kept because each is the accurate one in its own range: a long
+// run of steps that each keep most of the state (a near 1) has 1 - a far
+// below an ulp of 1, so a product of rounded a's loses it, while the sum of
+// the steps' complements keeps it to a few ulps; a run that forgets (c near
+// 1) has a tiny a that the product keeps and 1 - c does not.  This is the
+// log-space form's point (log(1 - z) = -softplus(k) carries the retained
+// fraction without the cancelling 1 - z) kept in linear arithmetic: the
+// composed state never needs a logarithm.
+struct Affine {
+  float a, c, b;
+};
+
 struct MinGRUOp {
-  static __device__ __forceinline__ Pair identity() { return {1.0f, 0.0f}; }
-  // The map "apply f, then s".
-  static __device__ __forceinline__ Pair compose(Pair f, Pair s) {
-    return {f.u * s.u, fmaf(s.u, f.v, s.v)};
+  using Step = Affine;  // one step's map, as the transform produces it
+  using Agg = Affine;   // a composed map
+  static __device__ __forceinline__ Agg identity() { return {1.0f, 0.0f, 0.0f}; }
+  // The coefficient of a composed map: 1 - C while C < 1/2 (A within half an
+  // ulp of 1's spacing, and C accurate to a few ulps), else the product A.
+  static __device__ __forceinline__ float coef(Agg f) { return f.c < 0.5f ? 1.0f - f.c : f.a; }
+  // Folds one step into a run (sequentially, in registers): "f, then s".
+  // C = C_f + A_f c_s adds non-negative terms, so it never cancels.
+  static __device__ __forceinline__ Agg push(Agg f, Step s) {
+    return {f.a * s.a, fmaf(f.a, s.c, f.c), fmaf(s.a, f.b, s.b)};
   }
+  // Composes two runs, "f, then s", each side's coefficient the accurate one.
+  static __device__ __forceinline__ Agg compose(Agg f, Agg s) {
+    const float fa = coef(f), sa = coef(s);
+    return {fa * sa, fmaf(fa, s.c, f.c), fmaf(sa, f.b, s.b)};
+  }
+  // The map a composed run applies (what phase 3 and the look-back words use).
+  static __device__ __forceinline__ Pair map(Agg f) { return {coef(f), f.b}; }
+  static __device__ __forceinline__ Pair step_map(Step s) { return {s.a, s.b}; }
   static __device__ __forceinline__ float apply(Pair m, float h) { return fmaf(m.u, h, m.v); }
-  // (k, p) -> (a, b) = (e^{-softplus(k)}, e^{log sigma(k) + log g(p)}).
-  // With e = e^{-|k|} in (0, 1]: sigma(|k|) = 1/(1+e), sigma(-|k|) = e/(1+e),
-  // so neither a nor z = sigma(k) is formed by a cancelling 1 - x.
-  static __device__ __forceinline__ Pair element(float k, float p) {
-    constexpr float kLog2e = 1.4426950408889634f;
-    const float e = __builtin_amdgcn_exp2f(-fabsf(k) * kLog2e);
-    const float big = __builtin_amdgcn_rcpf(1.0f + e);
-    const float small = e * big;
+  // (k, p) -> a = e^{-softplus(k)} = sigma(-k), its complement c = z =
+  // sigma(k), and b = e^{log z + log g(p)} = z g(p), without a cancelling
+  // 1 - x anywhere.  With e = e^{-|k|} and ep = e^{-|p|} in (0, 1]:
+  // sigma(|k|) = 1/(1+e), sigma(-|k|) = e/(1+e), and for p < 0,
+  // g(p) = sigma(p) = ep/(1+ep).  (1/(1+e) is exactly 1 when e is below half
+  // an ulp of 1, so a gate at rest keeps the state exactly.)  Every value is
+  // formed for both signs and selected, so the transform has no branch.
+  static __device__ __forceinline__ Step element(float k, float p) {
+    constexpr float kNegLog2e = -1.4426950408889634f;
+    const float e = __builtin_amdgcn_exp2f(fabsf(k) * kNegLog2e);
+    const float ep = __builtin_amdgcn_exp2f(fabsf(p) * kNegLog2e);
+    const float big = __builtin_amdgcn_rcpf(1.0f + e);  // 1 / (1 + e)
+    const float small = e * big;                        // e / (1 + e)
+    const float sig_p = ep * __builtin_amdgcn_rcpf(1.0f + ep);
     const bool kpos = k >= 0.0f;
     const float z = kpos ? big : small;
     const float a = kpos ? small : big;
-    // g(p) = p + 1/2 (p >= 0), sigma(p) = e^p / (1 + e^p) (p < 0).
-    const float ep = __builtin_amdgcn_exp2f(fminf(p, 0.0f) * kLog2e);
-    const float g = p >= 0.0f ? p + 0.5f : ep * __builtin_amdgcn_rcpf(1.0f + ep);
-    return {a, z * g};
+    const float g = p >= 0.0f ? p + 0.5f : sig_p;
+    return {a, z, z * g};
+  }
+  // The smaller of sigma(k) and sigma(-k) of a step: below the smallest
+  // normal fp32 number (|k| beyond ~87.3) it has flushed, and the term it
+  // multiplies is dropped.  Kernels keep the minimum of this over their steps
+  // and report out-of-range gates in the workspace status.  Both factors are
+  // non-negative, so their bit patterns order like their values (one integer
+  // min3 per step, and no NaN canonicalisation).
+  static __device__ __forceinline__ uint32_t gate_floor(Step s, uint32_t lo) {
+    const uint32_t x = __float_as_uint(s.a), y = __float_as_uint(s.c);
+    const uint32_t m = x < y ? x : y;
+    return lo < m ? lo : m;
+  }
+  static constexpr bool kHasGateRange = true;
+  // Time decay of the carried state: the step's coefficient a becomes a gamma
+  // with gamma = e^{-x}, and its complement 1 - a gamma = c + a (1 - gamma),
+  // where om = 1 - gamma must itself be accurate for small x (see decay_factors).
+  static __device__ __forceinline__ Step decayed(Step s, float gamma, float om) {
+    return {s.a * gamma, fmaf(s.a, om, s.c), s.b};
   }
 };
 
+// gamma = e^{-x} and 1 - gamma for x = rate * gap >= 0, both accurate: for
+// x < 1/8 the complement is the series x - x^2/2 + x^3/6 - x^4/24 + x^5/120
+// (truncation below 5e-8 relative), above it 1 - gamma no longer cancels
+// badly (gamma <= 0.883).  nx2 = -x log2(e).
+__device__ __forceinline__ void decay_factors(float nx2, float& gamma, float& om) {
+  constexpr float kLn2 = 0.6931471805599453f;
+  gamma = __builtin_amdgcn_exp2f(nx2);
+  const float x = -nx2 * kLn2;
+  const float series =
+      x * fmaf(x, fmaf(x, fmaf(x, fmaf(x, 1.0f / 120.0f, -1.0f / 24.0f), 1.0f / 6.0f), -0.5f), 1.0f);
+  om = x < 0.125f ? series : 1.0f - gamma;
+}
+
 struct MinMaxOp {
-  static __device__ __forceinline__ Pair identity() { return {INFINITY, -INFINITY}; }
-  static __device__ __forceinline__ Pair compose(Pair f, Pair s) {
+  using Step = Pair;
+  using Agg = Pair;
+  static __device__ __forceinline__ Agg identity() { return {INFINITY, -INFINITY}; }
+  // "f, then s": the clamp (min(R_f, R_s), max(min(R_s, S_f), S_s)).
+  static __device__ __forceinline__ Agg compose(Agg f, Agg s) {
     return {fminf(f.u, s.u), fmaxf(fminf(s.u, f.v), s.v)};
   }
+  static __device__ __forceinline__ Agg push(Agg f, Step s) { return compose(f, s); }
+  static __device__ __forceinline__ Pair map(Agg f) { return f; }
+  static __device__ __forceinline__ Pair step_map(Step s) { return s; }
   static __device__ __forceinline__ float apply(Pair m, float x) {
     return fmaxf(fminf(m.u, x), m.v);
   }
-  static __device__ __forceinline__ Pair element(float r, float s) { return {r, s}; }
+  static __device__ __forceinline__ Step element(float r, float s) { return {r, s}; }
+  static __device__ __forceinline__ uint32_t gate_floor(Step, uint32_t lo) { return lo; }
+  static constexpr bool kHasGateRange = false;
 };
 
 // ------------------------------------------------------------------ loads
@@ -235,7 +312,7 @@ __device__ float lookback_serial(const ScanParams& P, int64_t tchunk, int64_t b,
     }
     // Tile top - stop has not published yet: poll its word.
     if (++spins > P.spin_limit) {
-      __hip_atomic_store(P.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_or(P.status, kStatusTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       return __uint_as_float(kCanonNaN);
     }
     __builtin_amdgcn_s_sleep(8);  // ~512 cycles between polls of an unwritten word
@@ -294,7 +371,7 @@ __device__ __forceinline__ Tile decode_ticket(const ScanParams& P, uint32_t tick
 // threads in the workgroup (a multiple of Dc, at least Dc).
 template <class Op, int W, int Dc, int NT = 64 * W, int SB = kSerialBatch>
 __device__ __forceinline__ void resolve_tile(const ScanParams& P, const Tile& tl,
-                                             Pair (&s_pre)[W][Dc],
+                                             typename Op::Agg (&s_pre)[W][Dc],
                                              uint64_t (&s_win)[kWindowTiles][Dc],
                                              float (&s_hin)[Dc]) {
   const int kWin = P.window;  // in [1, kWindowTiles], uniform over the launch
@@ -303,11 +380,11 @@ __device__ __forceinline__ void resolve_tile(const ScanParams& P, const Tile& tl
   const int64_t dc = tl.d0 + tid;
   const bool chan_on = chan_thread && dc < P.D;
   const size_t plane = size_t(P.B) * size_t(P.D);  // words per tile index
-  Pair run = Op::identity();
+  typename Op::Agg run = Op::identity();
   if (chan_thread) {
 #pragma unroll
     for (int w = 0; w < W; ++w) {
-      const Pair a = s_pre[w][tid];
+      const typename Op::Agg a = s_pre[w][tid];
       s_pre[w][tid] = run;  // exclusive prefix of wave w
       run = Op::compose(run, a);
     }
@@ -317,7 +394,7 @@ __device__ __forceinline__ void resolve_tile(const ScanParams& P, const Tile& tl
     if (chan_on && P.init != nullptr) hin = P.init[size_t(tl.b) * P.D + dc];
   } else {
     if (chan_on)
-      store_word(P.state + size_t(tl.tchunk) * plane + size_t(tl.b) * P.D + dc, pack_map(run));
+      store_word(P.state + size_t(tl.tchunk) * plane + size_t(tl.b) * P.D + dc, pack_map(Op::map(run)));
     // All threads fetch the words of the kWin preceding tiles into LDS in
     // one round trip; position -1 stands for the initial state.
     const int c = tid % Dc;
@@ -360,7 +437,7 @@ __device__ __forceinline__ void resolve_tile(const ScanParams& P, const Tile& tl
     s_hin[tid] = hin;
     if (tl.tchunk + 1 < P.n_tchunks)
       store_word(P.state + size_t(tl.tchunk) * plane + size_t(tl.b) * P.D + dc,
-                 pack_state(Op::apply(run, hin)));
+                 pack_state(Op::apply(Op::map(run), hin)));
   }
   __syncthreads();
 }

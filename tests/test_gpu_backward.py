@@ -192,7 +192,7 @@ def test_mingru_backward_extreme_values():
     """Gate logits up to |k| = 87 (both sigmoids stay normal fp32 numbers),
     candidates up to 1e30, against the fp64 oracle with the conditioned
     errors (their floors keep outputs far below the fp32 range out of the
-    relative measure)."""
+    relative measure); the workspace status stays clear."""
     rng = np.random.default_rng(1140)
     B, T, D = 2, 2000, 130
     k = rng.choice([-87.0, -80.0, -30.0, -3.0, 0.0, 3.0, 30.0, 80.0, 87.0], (B, T, D)).astype(np.float32)
@@ -203,7 +203,34 @@ def test_mingru_backward_extreme_values():
     say("mingru bwd extremes")
     kd, pd, h0d = dev(k), dev(p), dev(h0)
     h = sr.mingru_forward(k=kd, p=pd, h0=h0d)
-    dk, dp, dh0 = sr.mingru_scan_backward(kd, pd, h, dev(dh), h0=h0d, dh_last=dev(dl))
+    ws = torch.empty(sr.raw_library().mingru_scan_backward_workspace_size(B, T, D),
+                     dtype=torch.uint8, device="cuda")
+    dk, dp, dh0 = sr.mingru_scan_backward(kd, pd, h, dev(dh), h0=h0d, dh_last=dev(dl), workspace=ws)
+    assert sr.workspace_status(ws) == sr.SR_OK
+    assert bool(torch.isfinite(dk).all() and torch.isfinite(dp).all() and torch.isfinite(dh0).all())
+    errs = _mingru_errors(k, p, h0, dh, dl, dk, dp, dh0)
+    say("errors", errs)
+    assert max(errs) < TOL, errs
+
+
+def test_mingru_backward_gate_logits_past_the_fp32_range():
+    """|k| up to 1e4 in the backward: the flushed factors drop terms below
+    1e-35 with moderate candidates and states, the gradients still meet the
+    bar, and the backward reports the range in its workspace status."""
+    rng = np.random.default_rng(1141)
+    B, T, D = 2, 2000, 130
+    k = rng.choice([-1e4, -100.0, -88.0, -4.0, 0.0, 4.0, 88.0, 100.0, 1e4], (B, T, D)).astype(np.float32)
+    p = rng.choice([-20.0, -1.0, 0.0, 1.0, 20.0, 1e3], (B, T, D)).astype(np.float32)
+    h0 = rng.choice([-1e3, -1.0, 0.0, 1.0, 1e3], (B, D)).astype(np.float32)
+    dh = rng.standard_normal((B, T, D)).astype(np.float32)
+    dl = rng.standard_normal((B, D)).astype(np.float32)
+    say("mingru bwd past the range")
+    kd, pd, h0d = dev(k), dev(p), dev(h0)
+    h = sr.mingru_forward(k=kd, p=pd, h0=h0d)
+    ws = torch.empty(sr.raw_library().mingru_scan_backward_workspace_size(B, T, D),
+                     dtype=torch.uint8, device="cuda")
+    dk, dp, dh0 = sr.mingru_scan_backward(kd, pd, h, dev(dh), h0=h0d, dh_last=dev(dl), workspace=ws)
+    assert sr.workspace_status(ws) == sr.SR_ERR_GATE_RANGE
     assert bool(torch.isfinite(dk).all() and torch.isfinite(dp).all() and torch.isfinite(dh0).all())
     errs = _mingru_errors(k, p, h0, dh, dl, dk, dp, dh0)
     say("errors", errs)

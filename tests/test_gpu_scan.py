@@ -210,35 +210,66 @@ def test_one_workspace_reused_across_shapes_and_ops():
         sr.mingru_scan_backward(kd, pd, h, torch.ones_like(h), workspace=ws)
 
 
-def test_chain_of_seven_thousand_tiles_closed_form():
+def _closed_form_check(B, T, D, kc, pc, h0, dtype):
+    """Constant k and p per channel: h_t = a^t h_0 + b (1 - a^t) / (1 - a), a =
+    sigma(-k), b = sigma(k) g(p) (a geometric series), at sampled steps of
+    every channel, conditioned as the oracle's error measure.  1 - a is
+    sigma(k) itself, so the series is evaluated without cancellation."""
+    k = torch.from_numpy(kc).cuda()[None, None, :].expand(B, T, D).to(dtype).contiguous()
+    p = torch.from_numpy(pc).cuda()[None, None, :].expand(B, T, D).to(dtype).contiguous()
+    kc64 = k[0, 0].double().cpu().numpy()  # the values the kernel reads
+    pc64 = p[0, 0].double().cpu().numpy()
+    y = sr.mingru_forward(k=k, p=p, h0=dev(h0))
+    del k, p
+    rng = np.random.default_rng([81, T])
+    ts = np.unique(np.concatenate([[1, 2, 143, 144, 145, 288, 289, 4096, T // 2, T - 1, T],
+                                   rng.integers(1, T + 1, 48)]))
+    got = host64(y[:, torch.from_numpy(ts - 1).to(y.device), :])
+    a = scalar.sigmoid(-kc64)
+    c = scalar.sigmoid(kc64)                                          # 1 - a
+    b = c * scalar.g(pc64)
+    # a^t = exp(-t softplus(k)) and 1 - a^t = -expm1(-t softplus(k)).
+    lt = ts[:, None].astype(np.float64) * scalar.softplus(kc64)[None, :]
+    at = np.exp(-lt)
+    carry = at[None] * h0.astype(np.float64)[:, None, :]
+    inp = (b * -np.expm1(-lt) / c)[None]
+    ref = carry + inp
+    err = np.max(np.abs(got - ref) / (np.abs(carry) + inp))
+    return err
+
+
+def test_long_memory_closed_form_across_thousands_of_tiles():
     """T = 2^20 + 5 in one chain per (batch row, channel tile): the state
-    crosses ~7300 tiles through the look-back.  With k and p constant per
-    channel the recurrence has the closed form h_t = a^t h_0 + b (1 - a^t) /
-    (1 - a), a = sigma(-k), b = sigma(k) g(p) (geometric series), checked in
-    fp64 at sampled steps, every channel.  D = 130: a ragged channel tile.
-    Memory lengths up to ~400 steps (k >= -6): near the fixed point b / c
-    (c = 1 - a) any fp32 evaluation is off by about ulp / c relative, since
-    a itself is held to an ulp (k = -8, c = 3.4e-4, gives ~1.4e-4)."""
+    crosses ~3600 tiles through the look-back.  Memory lengths up to
+    1/sigma(-12) ~ 1.6e5 steps (k in [-12, 2]), the regime where the
+    retained fraction 1 - sigma(k) is far below an ulp of 1: the scan carries
+    the complement of every composed coefficient, so the fixed point b/(1-a)
+    is reached to a few ulps (a product of rounded coefficients would be off
+    by ulp/(1-a), 1e-3 relative at k = -10).  D = 130: a ragged channel tile
+    (one channel per lane, 288-step tiles)."""
     B, T, D = 2, (1 << 20) + 5, 130
     say(f"closed form B={B} T={T} D={D}")
     rng = np.random.default_rng(81)
-    kc = rng.uniform(-6.0, 2.0, D).astype(np.float32)    # memory from ~400 steps to ~1
+    kc = np.concatenate([[-12.0, -11.0, -10.0, -9.0, -8.0, -6.0, -4.0, 2.0],
+                         rng.uniform(-12.0, 2.0, D - 8)]).astype(np.float32)
     pc = rng.standard_normal(D).astype(np.float32)
     h0 = rng.standard_normal((B, D)).astype(np.float32)
-    k = torch.from_numpy(kc).cuda()[None, None, :].expand(B, T, D).contiguous()
-    p = torch.from_numpy(pc).cuda()[None, None, :].expand(B, T, D).contiguous()
-    y = sr.mingru_forward(k=k, p=p, h0=dev(h0))
-    del k, p
-    ts = np.unique(np.concatenate([[1, 2, 143, 144, 145, 288, 289, 4096, 1 << 19, T - 1, T],
-                                   rng.integers(1, T + 1, 48)]))
-    got = host64(y[:, torch.from_numpy(ts - 1).to(y.device), :])
-    a = scalar.sigmoid(-kc.astype(np.float64))
-    b = scalar.sigmoid(kc.astype(np.float64)) * scalar.g(pc.astype(np.float64))
-    at = np.power(a[None, :], ts[:, None].astype(np.float64))          # [n_t, D]
-    carry = at[None] * h0.astype(np.float64)[:, None, :]
-    inp = (b * (1.0 - at) / (1.0 - a))[None]
-    ref = carry + inp
-    err = np.max(np.abs(got - ref) / (np.abs(carry) + inp))
+    err = _closed_form_check(B, T, D, kc, pc, h0, torch.float32)
+    say("closed-form error", err)
+    assert err < TOL_F32
+
+
+def test_long_memory_closed_form_two_channels_per_lane():
+    """The same closed form on the other tile geometry (two channels per lane,
+    144-step tiles, 64 chains) with bf16 gate logits, k in [-12, 2], over
+    2^17 steps (~900 tiles per chain)."""
+    B, T, D = 32, 1 << 17, 256
+    say(f"closed form B={B} T={T} D={D} bf16")
+    rng = np.random.default_rng(83)
+    kc = np.concatenate([[-12.0, -10.0, -8.0, 2.0], rng.uniform(-12.0, 2.0, D - 4)]).astype(np.float32)
+    pc = rng.standard_normal(D).astype(np.float32)
+    h0 = rng.standard_normal((B, D)).astype(np.float32)
+    err = _closed_form_check(B, T, D, kc, pc, h0, torch.bfloat16)
     say("closed-form error", err)
     assert err < TOL_F32
 

@@ -106,10 +106,8 @@ def test_extreme_gate_and_candidate_values():
     """Gate logits deep into both saturations, candidates from -1e4 to 1e30
     and carried states up to 1e20, against the fp64 oracle: no NaN, no
     overflow, the conditioned error within the fp32 bar.  For |k| <= 87 both
-    sigma(k) and sigma(-k) are normal fp32 numbers; beyond, the smaller one
-    flushes to zero and the term it multiplies is dropped -- invisible unless
-    that term is enormous (the documented limit of the closed-form
-    coefficients), so |k| stops at 87 here."""
+    sigma(k) and sigma(-k) are normal fp32 numbers, so no term is dropped and
+    the workspace status stays clear."""
     rng = np.random.default_rng(1600)
     B, T, D = 2, 3000, 130
     k_vals = np.array([-87.0, -80.0, -30.0, -3.0, 0.0, 3.0, 30.0, 80.0, 87.0])
@@ -118,7 +116,10 @@ def test_extreme_gate_and_candidate_values():
     p = rng.choice(p_vals, (B, T, D)).astype(np.float32)
     h0 = rng.choice([-1e20, -1.0, 0.0, 1.0, 1e20], (B, D)).astype(np.float32)
     say("extreme values")
-    h = sr.mingru_forward(k=dev(k), p=dev(p), h0=dev(h0))
+    ws = torch.empty(sr.raw_library().mingru_forward_workspace_size(B, T, 0, D, D, 0, 0),
+                     dtype=torch.uint8, device="cuda")
+    h = sr.mingru_forward(k=dev(k), p=dev(p), h0=dev(h0), workspace=ws)
+    assert sr.workspace_status(ws) == sr.SR_OK
     assert bool(torch.isfinite(h).all())
     # Outputs far below the fp32 normal range (e.g. sigma(-100) = 4e-44) are
     # flushed to zero: the error is measured against at least 1e-30.
@@ -127,3 +128,74 @@ def test_extreme_gate_and_candidate_values():
     err = metrics.h_rel_err(host64(h), h_ref, carry, inp, floor=1e-30)
     say("error", err)
     assert err < TOL_F32
+
+
+def test_gate_logits_past_the_fp32_range():
+    """|k| up to 1e4: beyond ~87.3 the smaller of sigma(k), sigma(-k) flushes
+    to zero in fp32 and the term it multiplies is dropped, which the scan
+    reports (SR_ERR_GATE_RANGE) while still writing finite results.  With
+    candidates and states of moderate size the dropped terms are below
+    1e-35, so the results still meet the bar against the fp64 oracle."""
+    rng = np.random.default_rng(1601)
+    B, T, D = 2, 3000, 130
+    k_vals = np.array([-1e4, -300.0, -100.0, -88.0, -87.0, -4.0, 0.0, 4.0, 87.0, 88.0, 100.0,
+                       300.0, 1e4])
+    k = rng.choice(k_vals, (B, T, D)).astype(np.float32)
+    p = rng.choice([-20.0, -1.0, 0.0, 1.0, 20.0, 1e3], (B, T, D)).astype(np.float32)
+    h0 = rng.choice([-1e3, -1.0, 0.0, 1.0, 1e3], (B, D)).astype(np.float32)
+    say("gate logits past the fp32 range")
+    ws = torch.empty(sr.raw_library().mingru_forward_workspace_size(B, T, 0, D, D, 0, 0),
+                     dtype=torch.uint8, device="cuda")
+    h = sr.mingru_forward(k=dev(k), p=dev(p), h0=dev(h0), workspace=ws)
+    assert sr.workspace_status(ws) == sr.SR_ERR_GATE_RANGE
+    assert bool(torch.isfinite(h).all())
+    h_ref = mingru.scan(k, p, h0)
+    carry, inp = mingru.scan_terms(k, p, h0)
+    err = metrics.h_rel_err(host64(h), h_ref, carry, inp, floor=1e-30)
+    say("error", err)
+    assert err < TOL_F32
+    # The same inputs with every |k| clipped to 87 are inside the range.
+    kc = np.clip(k, -87.0, 87.0)
+    sr.mingru_forward(k=dev(kc), p=dev(p), h0=dev(h0), workspace=ws)
+    assert sr.workspace_status(ws) == sr.SR_OK
+
+
+def test_dropped_term_is_reported():
+    """Where the dropped term is the whole signal -- every gate at k = -100
+    (sigma(k) = 3.7e-44, below the fp32 normal range) with candidates of 1e30
+    from a zero state, so that h_t = t * 3.7e-14 in fp64 -- the fp32 result
+    loses it (zero, or what is left of a subnormal factor), and the status
+    says why.  One channel in range alongside is unaffected."""
+    B, T, D = 1, 500, 64
+    k = np.full((B, T, D), -100.0, np.float32)
+    p = np.full((B, T, D), 1e30, np.float32)
+    k[..., 0] = -2.0
+    p[..., 0] = 1.0
+    ws = torch.empty(sr.raw_library().mingru_forward_workspace_size(B, T, 0, D, D, 0, 0),
+                     dtype=torch.uint8, device="cuda")
+    h = sr.mingru_forward(k=dev(k), p=dev(p), workspace=ws)
+    assert sr.workspace_status(ws) == sr.SR_ERR_GATE_RANGE
+    lost = host64(h[..., 1:])
+    full = mingru.scan(k[..., 1:2], p[..., 1:2])
+    assert np.all(np.isfinite(lost)) and np.all(lost >= 0) and np.all(lost <= full * (1 + 1e-6))
+    ref = mingru.scan(k[..., :1], p[..., :1])
+    assert np.max(np.abs(host64(h[..., :1]) - ref) / ref) < TOL_F32
+
+
+@pytest.mark.parametrize("T", [512, 65536])  # the GEMM + scan path, and the fused one
+def test_gate_range_reported_through_the_layer(T):
+    """A layer forward whose projection produces gate logits past the range
+    (a weight column of 1e3 on inputs of size ~1) reports it too, on the
+    fused path (2 x 65536 x 64: 512 tiles) and the unfused one."""
+    B, D_in, D = 2, 16, 64
+    rng = np.random.default_rng([1602, T])
+    x = rng.standard_normal((B, T, D_in)).astype(np.float32)
+    W = (rng.standard_normal((D_in, 2 * D)) / 4).astype(np.float32)
+    nb = sr.raw_library().mingru_forward_workspace_size(B, T, D_in, D, D, 1, 0)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    sr.mingru_forward(dev(x), dev(W), workspace=ws)
+    assert sr.workspace_status(ws) == sr.SR_OK
+    W[:, 5] = 1e3
+    y = sr.mingru_forward(dev(x), dev(W), workspace=ws)
+    assert sr.workspace_status(ws) == sr.SR_ERR_GATE_RANGE
+    assert bool(torch.isfinite(y).all())
