@@ -161,10 +161,13 @@ def test_minmax_backward_hold_and_reset():
     assert torch.count_nonzero(ds) == B * D
 
 
-def test_full_size_b8_t65536_d1024_backward_sampled():
+def test_full_size_b8_t65536_d1024_backward_every_element():
+    """The backward at the bench workload's full size: dk, dp and dh0 of every
+    channel and step against the fp64 oracle's gradients (worker processes)."""
+    from tests import fullsize
     cfg = synth.CONFIGS[synth.SCAN]
     B, T, D = cfg["B"], cfg["T"], cfg["D"]
-    say("full size B=8 T=65536 D=1024 backward")
+    say("full size B=8 T=65536 D=1024 backward, every element")
     kb = synth.device_normal(synth.SCAN, "k", (B, T, D), cfg["k_mean"], cfg["k_std"], torch.bfloat16)
     pb = synth.device_normal(synth.SCAN, "p", (B, T, D), cfg["p_mean"], cfg["p_std"], torch.bfloat16)
     h0 = synth.device_normal(synth.SCAN, "h0", (B, D))
@@ -177,14 +180,14 @@ def test_full_size_b8_t65536_d1024_backward_sampled():
     dk, dp, dh0 = sr.mingru_scan_backward(kb, pb, h, dh, h0=h0, workspace=ws)
     assert sr.workspace_status(ws) == 0
     assert bool(torch.isfinite(dk).all()) and bool(torch.isfinite(dp).all())
-    rng = np.random.default_rng(1131)
-    bs = torch.as_tensor(rng.integers(0, B, 12), device="cuda")
-    ds_ = torch.as_tensor(rng.integers(0, D, 12), device="cuda")
-    pick = lambda x: x[bs, :, ds_].double().cpu().numpy()[None].transpose(0, 2, 1)
-    errs = _mingru_errors(pick(kb), pick(pb), h0[bs, ds_].double().cpu().numpy()[None],
-                          pick(dh), None, dk[bs, :, ds_][None].transpose(1, 2),
-                          dp[bs, :, ds_][None].transpose(1, 2), dh0[bs, ds_][None])
-    say("full size backward errors", errs)
+    H = fullsize.host32
+    arrays = dict(k=H(kb), p=H(pb), h0=H(h0), dh=H(dh), dk=H(dk), dp=H(dp), dh0=H(dh0))
+    del kb, pb, h, dh, dk, dp
+    torch.cuda.empty_cache()
+    say("oracle gradients on every channel")
+    res = fullsize.all_channels(fullsize.backward_slice_errors, arrays, B, D)
+    errs = tuple(max(r[i] for r in res) for i in range(3))
+    say("full size backward errors (every element)", errs)
     assert max(errs) < 1e-4, errs
 
 

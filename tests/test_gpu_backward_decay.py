@@ -100,12 +100,14 @@ def test_zero_rate_equals_undecayed_backward_bitwise():
         assert torch.equal(a, b)
 
 
-def test_full_size_b8_t65536_d1024_decayed_backward_sampled():
-    """The decayed scan's backward at the headline scan's shape (bf16 k/p),
-    12 sampled channels checked over all 65536 steps."""
+def test_full_size_b8_t65536_d1024_decayed_backward_every_element():
+    """The decayed scan's backward at the headline scan's shape (bf16 k/p):
+    dk, dp and dh0 of every channel and step against the fp64 oracle's
+    gradients (worker processes)."""
+    from tests import fullsize
     cfg = synth.CONFIGS[synth.SCAN]
     B, T, D = cfg["B"], cfg["T"], cfg["D"]
-    say("decayed bwd full size B=8 T=65536 D=1024 sampled")
+    say("decayed bwd full size B=8 T=65536 D=1024, every element")
     kb = synth.device_normal(synth.SCAN, "k", (B, T, D), cfg["k_mean"], cfg["k_std"], torch.bfloat16)
     pb = synth.device_normal(synth.SCAN, "p", (B, T, D), cfg["p_mean"], cfg["p_std"], torch.bfloat16)
     h0 = synth.device_normal(synth.SCAN, "h0", (B, D))
@@ -122,18 +124,16 @@ def test_full_size_b8_t65536_d1024_decayed_backward_sampled():
                                                   decay_rate=lam, delta_t=gap)
     assert sr.workspace_status(ws) == 0
     assert bool(torch.isfinite(dk).all()) and bool(torch.isfinite(dp).all())
-    rng = np.random.default_rng(1302)
-    errs = []
-    for b in rng.choice(B, 2, replace=False):
-        ds = torch.as_tensor(np.sort(rng.choice(D, 6, replace=False)), device="cuda")
-        sl = lambda t: t[b][:, ds].double().cpu().numpy()[None]   # [1, T, 6]
-        e = _decay_errors(sl(kb), sl(pb), h0[b][ds].double().cpu().numpy()[None], sl(dh),
-                          dl[b][ds].double().cpu().numpy()[None], lam[ds].double().cpu().numpy(),
-                          gap[b:b + 1].double().cpu().numpy(), False,
-                          dk[b][:, ds][None], dp[b][:, ds][None], dh0[b][ds][None])
-        errs.append(max(e))
-    say("sampled errors", max(errs))
-    assert max(errs) < TOL
+    H = fullsize.host32
+    arrays = dict(k=H(kb), p=H(pb), h0=H(h0), dh=H(dh), dh_last=H(dl), dk=H(dk), dp=H(dp),
+                  dh0=H(dh0), lam=H(lam), dt=H(gap), log1p=np.zeros(1, np.int32))
+    del kb, pb, h, dh, dk, dp
+    torch.cuda.empty_cache()
+    say("oracle gradients on every channel")
+    res = fullsize.all_channels(fullsize.backward_slice_errors, arrays, B, D)
+    errs = tuple(max(r[i] for r in res) for i in range(3))
+    say("decayed backward errors (every element)", errs)
+    assert max(errs) < TOL, errs
 
 
 @pytest.mark.parametrize("decayed", [False, True])

@@ -186,10 +186,13 @@ def test_decayed_step_loop_matches_oracle():
     assert metrics.y_rel_err(host64(y), y_ref, hs_ref, W_out) < 1e-4
 
 
-def test_full_size_b8_t65536_d1024_decayed_sampled():
+def test_full_size_b8_t65536_d1024_decayed_every_element():
+    """The decayed scan at the bench workload's full size, with gaps that
+    saturate: every output against the fp64 oracle (worker processes)."""
+    from tests import fullsize
     cfg = synth.CONFIGS[synth.SCAN]
     B, T, D = cfg["B"], cfg["T"], cfg["D"]
-    say("decay full size B=8 T=65536 D=1024")
+    say("decay full size B=8 T=65536 D=1024, every element")
     kb = synth.device_normal(synth.SCAN, "k", (B, T, D), cfg["k_mean"], cfg["k_std"], torch.bfloat16)
     pb = synth.device_normal(synth.SCAN, "p", (B, T, D), cfg["p_mean"], cfg["p_std"], torch.bfloat16)
     h0 = synth.device_normal(synth.SCAN, "h0", (B, D))
@@ -202,17 +205,15 @@ def test_full_size_b8_t65536_d1024_decayed_sampled():
                                   saturated=sat, workspace=ws)
     assert sr.workspace_status(ws) == 0
     assert int(sat.item()) == 1
-    rng = np.random.default_rng(1204)
-    bs = rng.integers(0, B, 12)
-    ds = rng.integers(0, D, 12)
-    errs = []
-    for b, d in zip(bs, ds):
-        kc = kb[b, :, d].double().cpu().numpy()[None, :, None]
-        pc = pb[b, :, d].double().cpu().numpy()[None, :, None]
-        h0c = h0[b, d].double().cpu().numpy().reshape(1, 1)
-        errs.append(_err(h[b, :, d][None, :, None], kc, pc, lam[d:d + 1], dt[b:b + 1], h0c, False))
-    say("sampled errors", max(errs))
-    assert max(errs) < TOL_F32
+    H = fullsize.host32
+    arrays = dict(k=H(kb), p=H(pb), h0=H(h0), got=H(h), lam=lam, dt=dt,
+                  log1p=np.zeros(1, np.int32))
+    del kb, pb, h
+    torch.cuda.empty_cache()
+    say("oracle on every channel")
+    err = max(fullsize.all_channels(fullsize.decayed_slice_error, arrays, B, D))
+    say("decayed full size error (every element)", err)
+    assert err < TOL_F32
 
 
 def test_decayed_step_over_many_streams():

@@ -126,10 +126,13 @@ def test_layer_object_api():
 
 def test_decode_b256_d2048():
     """Decode workload: B=256 streams, D=2048; a parallel prefill of 512 steps, then
-    4096 single-token steps carrying h.  The final state must match the
-    parallel forward over the concatenated 4608-step sequence; two seeded
-    rows are also checked against the fp64 oracle after steps 1, 2, 8 and at
-    the end (the prefill's carry is still visible in the first steps)."""
+    4096 single-token steps carrying h.  Every one of the 256 rows is checked
+    against the fp64 oracle after steps 1, 2, 8 (where the prefill's carry is
+    still visible) and at the end; the oracle runs the whole 4608-step
+    sequence, its projections (fp64 BLAS) streamed by blocks of 512 steps.
+    The final state must also match the parallel forward over the
+    concatenated sequence."""
+    from oracle import mingru as orc
     cfg = synth.CONFIGS[synth.STEP]
     B, D, Tp, S = cfg["B"], cfg["D"], cfg["T_prefill"], cfg["steps"]
     say("decode B=256 D=2048")
@@ -137,30 +140,37 @@ def test_decode_b256_d2048():
     W_out = synth.device_normal(synth.STEP, "W_out", (D, D), 0.0, cfg["w_std"])
     x = synth.device_normal(synth.STEP, "x", (B, Tp + S, D))
     _, h = sr.mingru_forward(x[:, :Tp], W_in, W_out=W_out, return_last=True)
-    rows = [3, 201]
+    checks = (1, 2, 8)
     snaps = {}
     for t in range(S):
         y_t, h = sr.mingru_step(x[:, Tp + t].contiguous(), W_in, W_out, h_prev=h)
-        if t + 1 in (1, 2, 8):
-            snaps[t + 1] = h[rows].double().cpu().numpy()
+        if t + 1 in checks:
+            snaps[Tp + t + 1] = h.double().cpu().numpy()
+    snaps[Tp + S] = h.double().cpu().numpy()
     y_full, h_full = sr.mingru_forward(x, W_in, W_out=W_out, return_last=True)
     rel = float((h - h_full).abs().max() / h_full.abs().max())
     say("decode vs parallel", rel)
     assert rel < 1e-4
-    # Oracle on two rows in fp64: the whole 4608-step sequence run
-    # sequentially (the projections of every step are one matmul).
-    xr = x[rows].double().cpu().numpy()
+    # The oracle on all rows: h_t for t = 1 .. 4608 from the zero state, one
+    # block of 512 steps at a time (the block's projection, then the scan
+    # from the state the previous block left).
     Wi = W_in.double().cpu().numpy()
-    _, h_all, _ = mingru.layer(xr, Wi, None)
+    ref = {}
+    state = None
+    blk = synth.T_BLOCK
+    for t0 in range(0, Tp + S, blk):
+        xb = x[:, t0:t0 + blk].double().cpu().numpy()
+        k, p = orc.layer_kp(xb, Wi)
+        hb = orc.scan(k, p, state)
+        for step in snaps:
+            if t0 < step <= t0 + blk:
+                ref[step] = hb[:, step - 1 - t0].copy()
+        state = hb[:, -1].copy()
+        say(f"decode oracle: steps {t0 + 1}..{t0 + blk} done")
     for step, got in snaps.items():
-        ref = h_all[:, Tp + step - 1]
-        e = np.max(np.abs(got - ref) / np.abs(ref))
-        say("decode step", step, "err", e)
-        assert e < TOL_F32
-    ref = h_all[:, -1]
-    e = np.max(np.abs(h[rows].double().cpu().numpy() - ref) / np.abs(ref))
-    say("decode final err", e)
-    assert e < TOL_F32
+        e = float(np.max(np.abs(got - ref[step]) / np.abs(ref[step])))
+        say("decode step", step, "all rows, err", e)
+        assert e < TOL_F32, (step, e)
 
 
 @pytest.mark.parametrize("B,T,D_h,D_out", [
