@@ -39,7 +39,9 @@
  * - All tensor pointers are DEVICE pointers; the caller owns every buffer,
  *   including the workspace.  The library keeps no pointer after a call
  *   returns and holds no global mutable state except a thread-local error
- *   string and the look-back poll bound (scanrnn_set_lookback_spin_limit).
+ *   string, the look-back poll bound (scanrnn_set_lookback_spin_limit) and
+ *   the device array of mingru_scan_noalloc (with the caller-owned-buffer
+ *   rule its one exception).
  * - Tensors are row-major, innermost (feature) dimension fastest; a [B,T,D]
  *   tensor is B*T rows of D elements.  Pointers must be aligned to their
  *   element size; wider alignment (8 or 16 bytes) lets the library use
@@ -261,6 +263,28 @@ sr_status minmax_scan_backward(int64_t B, int64_t T, int64_t D,
                                const float* x_out, const float* dx, const float* dx_last,
                                float* dr, float* ds, float* dx0,
                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The scan-only mingru_forward (W_in and W_out NULL, y = h) for callers that
+ * cannot allocate -- code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc: no workspace argument and no allocation
+ * of any kind.  Its look-back words live in a fixed device array of
+ * mingru_scan_noalloc_max_workspace() bytes (32 MiB), one per GPU, held
+ * until the process ends; requests needing more (scan workspace above that:
+ * B * ceil(T/144) * D * 8 + 256 bytes) return SR_ERR_UNSUPPORTED before any
+ * HIP call.  Every call on a GPU shares that GPU's array and resets it
+ * first, on `stream`: calls in one stream are ordered and safe, calls that
+ * overlap on one GPU (several streams, several host threads) race.  Results
+ * are those of mingru_forward on the same inputs, bit for bit.  The first
+ * call on a device looks up that device's copy of the array.
+ *
+ *   k, p, ld_kp, kp_dtype, h0   as in mingru_forward (scan-only use).
+ *   h       [B,T,D] fp32 output;  h_last [B,D] fp32 or NULL.
+ */
+size_t mingru_scan_noalloc_max_workspace(void);
+sr_status mingru_scan_noalloc(int64_t B, int64_t T, int64_t D,
+                              const void* k, const void* p, int64_t ld_kp, sr_dtype kp_dtype,
+                              const float* h0, float* h, float* h_last, void* stream);
 
 /* Text of the last non-OK status returned on this thread ("" if none). */
 const char* scanrnn_last_error(void);

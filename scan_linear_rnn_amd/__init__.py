@@ -71,6 +71,8 @@ EXPORTED = (
     "mingru_scan_backward_decayed",
     "minmax_scan_backward_workspace_size",
     "minmax_scan_backward",
+    "mingru_scan_noalloc_max_workspace",
+    "mingru_scan_noalloc",
     "scanrnn_last_error",
     "scanrnn_set_lookback_spin_limit",
     "scanrnn_workspace_status",
@@ -129,6 +131,10 @@ def _load() -> ctypes.CDLL:
     lib.minmax_scan_backward.restype = i32
     lib.minmax_scan_backward.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                          sz, vp]
+    lib.mingru_scan_noalloc_max_workspace.restype = sz
+    lib.mingru_scan_noalloc_max_workspace.argtypes = []
+    lib.mingru_scan_noalloc.restype = i32
+    lib.mingru_scan_noalloc.argtypes = [i64, i64, i64, vp, vp, i64, i32, vp, vp, vp, vp]
     lib.scanrnn_last_error.restype = ctypes.c_char_p
     lib.scanrnn_last_error.argtypes = []
     lib.scanrnn_set_lookback_spin_limit.restype = i32

@@ -312,6 +312,8 @@ sr_status mingru_backward_impl(int64_t B, int64_t T, int64_t D, const void* k, c
 
 }  // namespace
 
+void clear_last_error() { g_last_error[0] = '\0'; }
+
 sr_status fail(sr_status code, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);

@@ -14,6 +14,9 @@ namespace sr {
 // returns `code`.
 sr_status fail(sr_status code, const char* fmt, ...);
 
+// Empties the calling thread's last-error text (each entry point starts so).
+void clear_last_error();
+
 // Polls of an unwritten look-back word after which a scan gives up (marks
 // the workspace, publishes NaN): process-wide, SCANRNN_LOOKBACK_SPIN_LIMIT
 // unless scanrnn_set_lookback_spin_limit lowered it.

@@ -276,3 +276,21 @@ int main(void) {
 
 def lib_version():
     return lib.scanrnn_version().decode()
+
+
+def test_no_alloc_scan_validates_before_any_hip_call():
+    """mingru_scan_noalloc refuses bad sizes and requests beyond its device
+    array before touching the GPU (so this runs without one)."""
+    assert lib.mingru_scan_noalloc_max_workspace() == 32 << 20
+    st = lib.mingru_scan_noalloc(8, 1 << 17, 1024, FAKE, FAKE2, 1024, sr.SR_BF16, None, FAKE,
+                                 None, None)
+    assert st == sr.SR_ERR_UNSUPPORTED
+    assert b"no-alloc scratch" in lib.scanrnn_last_error()
+    assert lib.mingru_scan_noalloc(-1, 4, 4, FAKE, FAKE2, 4, sr.SR_F32, None, FAKE, None,
+                                   None) == sr.SR_ERR_INVALID_ARGUMENT
+    assert lib.mingru_scan_noalloc(2, 4, 8, FAKE, FAKE2, 4, sr.SR_F32, None, FAKE, None,
+                                   None) == sr.SR_ERR_INVALID_ARGUMENT   # ld_kp < D
+    assert lib.mingru_scan_noalloc(2, 4, 8, None, FAKE2, 8, sr.SR_F32, None, FAKE, None,
+                                   None) == sr.SR_ERR_INVALID_ARGUMENT   # k missing
+    assert lib.mingru_scan_noalloc(2, 4, 8, FAKE, FAKE2, 8, 7, None, FAKE, None,
+                                   None) == sr.SR_ERR_INVALID_ARGUMENT   # dtype
