@@ -82,7 +82,11 @@ typedef enum {
   SR_ERR_GATE_RANGE = 6          /* reported by scanrnn_workspace_status only   */
 } sr_status;
 
-typedef enum { SR_F32 = 0, SR_BF16 = 1 } sr_dtype;
+/* Element type of k and p: one of these values, passed as a 32-bit integer
+ * so that whatever a caller sends is a valid value of the type; any other
+ * value is rejected with SR_ERR_INVALID_ARGUMENT. */
+enum { SR_F32 = 0, SR_BF16 = 1 };
+typedef int32_t sr_dtype;
 
 /* Bytes of workspace mingru_forward needs.  has_w_in / has_w_out say whether
  * the call will pass W_in / W_out.  W_out needs B*T*D_h floats to stage h.

@@ -43,7 +43,9 @@ __all__ = [
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_PKG, "libscanrnn.so")
+# SCANRNN_LIBRARY names another build of the same library to load instead of
+# the in-tree one (the host-sanitizer build of build.py uses it).
+_LIB_PATH = os.environ.get("SCANRNN_LIBRARY") or os.path.join(_PKG, "libscanrnn.so")
 
 SR_OK = 0
 SR_ERR_INVALID_ARGUMENT = 1
