@@ -32,6 +32,10 @@ carries:
                 loop, and the read+write streaming ceiling (the faster of
                 the device copy and an elementwise kernel with the same
                 traffic; roofline.frac_of_copy_ceiling is relative to it).
+                Opt-in (name them in --legs): shapes -- one scan call over
+                the sweep shapes (both operators, bf16 and fp32 inputs);
+                streams -- read-only, write-only and read+write ceilings of
+                torch's own kernels on 2 GiB.
 
 The headline scan is measured last, after the other legs, on a GPU already
 at its sustained clock.  Only one GPU is used; --gpus above 1 exits with a
@@ -489,6 +493,76 @@ def leg_copy(torch):
                 elementwise_GBps=elem_gbps)
 
 
+# Scan shapes of the sweep table: (B, T, D, input dtype, operator).
+SHAPE_SWEEP = [
+    (8, 65536, 1024, "bf16", "mingru"), (64, 8192, 1024, "bf16", "mingru"),
+    (8, 16384, 4096, "bf16", "mingru"), (32, 65536, 256, "bf16", "mingru"),
+    (128, 65536, 64, "bf16", "mingru"), (1, 524288, 1024, "bf16", "mingru"),
+    (8, 4096, 1024, "bf16", "mingru"), (8, 1024, 1024, "bf16", "mingru"),
+    (2, 1024, 512, "bf16", "mingru"), (8, 16384, 4096, "f32", "mingru"),
+    (1, 65536, 1024, "bf16", "mingru"), (8, 65536, 128, "bf16", "mingru"),
+    (8, 8192, 1024, "bf16", "mingru"),
+    (8, 65536, 1024, "f32", "minmax"), (1, 262144, 192, "f32", "minmax"),
+    (1, 32768, 192, "f32", "minmax"),
+]
+
+
+def leg_shapes(torch, sr, synth, steps, warmup):
+    """One scan call (workspace reset included) over the sweep shapes: median
+    of the HIP events, and the algorithmic bytes over it (minGRU: k, p in,
+    h out; MinMax: r, s in, x out; plus h0 and h_T)."""
+    lib = sr.raw_library()
+    res = {}
+    for B, T, D, dt, op in SHAPE_SWEEP:
+        tag = f"{op}_{B}x{T}x{D}_{dt}"
+        log(f"[bench] shapes: {tag}")
+        dtype = torch.bfloat16 if dt == "bf16" else torch.float32
+        esz = 2 if dt == "bf16" else 4
+        if op == "mingru":
+            a = synth.device_normal(synth.SCAN, "k_" + tag, (B, T, D), -2.0, 1.5, dtype)
+            b = synth.device_normal(synth.SCAN, "p_" + tag, (B, T, D), 0.0, 1.0, dtype)
+            h0 = synth.device_normal(synth.SCAN, "h0_" + tag, (B, D))
+            ws = torch.empty(lib.mingru_forward_workspace_size(B, T, 0, D, D, 0, 0),
+                             dtype=torch.uint8, device="cuda")
+            fn = lambda: sr.mingru_forward(k=a, p=b, h0=h0, workspace=ws)
+        else:
+            a = synth.device_uniform(synth.MINMAX, "r_" + tag, (B, T, D), -1.0, 1.0)
+            b = synth.device_uniform(synth.MINMAX, "s_" + tag, (B, T, D), -1.5, 0.5)
+            h0 = synth.device_uniform(synth.MINMAX, "x0_" + tag, (B, D), -1.0, 1.0)
+            ws = torch.empty(lib.minmax_scan_workspace_size(B, T, D), dtype=torch.uint8,
+                             device="cuda")
+            fn = lambda: sr.minmax_scan(a, b, h0, workspace=ws)
+        _, per = time_launches(torch, fn, steps, warmup)
+        alg = B * T * D * (2 * esz + 4) + 2 * B * D * 4
+        med = median(per)
+        res[tag] = {"launch_ms_median": med, "launch_ms_min": min(per),
+                    "frac_of_hbm_peak": round(alg / (med * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+        del a, b, h0, ws
+        torch.cuda.empty_cache()
+    return res
+
+
+def leg_streams(torch):
+    """Streaming ceilings on 2 GiB fp32 buffers with torch's own kernels:
+    read-only (a sum), write-only (a fill), read + write (copy, and an
+    elementwise negation); GB/s over the median launch."""
+    n = 1 << 29
+    a = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    r = torch.empty((), dtype=torch.float32, device="cuda")
+    nb = 4 * n
+    out = {}
+    for name, fn, nbytes in [("read_sum", lambda: torch.sum(a, out=r), nb),
+                             ("write_fill", lambda: b.fill_(2.0), nb),
+                             ("copy", lambda: b.copy_(a), 2 * nb),
+                             ("elementwise_neg", lambda: torch.neg(a, out=b), 2 * nb)]:
+        med = median(time_launches(torch, fn, 40, 3)[1])
+        out[name] = {"GBps": round(nbytes / (med * 1e-3) / 1e9, 1), "launch_ms_median": med}
+    del a, b
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[1])
     ap.add_argument("--gpus", type=int, default=1)
@@ -542,6 +616,10 @@ def main():
         extra["step_b256_d2048"] = leg_decode(torch, sr, synth, args.decode_steps)
     if "minmax_step" in legs:
         extra["minmax_step_b8_d192"] = leg_minmax_step(torch, sr, synth, 4096)
+    if "shapes" in legs:
+        extra["scan_shapes"] = leg_shapes(torch, sr, synth, 20, 5)
+    if "streams" in legs:
+        extra["stream_ceilings"] = leg_streams(torch)
     if "copy" in legs:
         extra["copy_ceiling"] = leg_copy(torch)
     if "scan" in legs:

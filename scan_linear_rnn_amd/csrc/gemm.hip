@@ -215,13 +215,25 @@ constexpr int kNarrowMaxM = 512;
 // D=1024 81 -> 68 us; with K = 2048 (B=2 T=1024 D=2048) 449 -> 456 us.
 constexpr int kNarrowWideMaxM = 4096;
 constexpr int kNarrowWideMaxK = 1024;
-constexpr int kNarrowKG = 8;  // waves (K groups) per workgroup
 constexpr int kNarrowSK = 16; // K per pipeline stage
+
+// Waves (K groups) per workgroup and stage buffers per wave, by tile height.
+// A wave keeps kStages - 1 stages loading while it multiplies one: a stage
+// holds only 32 (64-row tiles) or 16 (32-row tiles) MFMAs per wave, too
+// short to cover a load's latency alone.  For 64-row tiles deeper prefetch
+// beats more waves: four waves with three stages each (one wave per SIMD)
+// against eight waves that fit only two (step B=256 D=2048, x_t W_in:
+// 41.7 -> 36.9 us; a fourth stage, operands read into registers a half
+// stage ahead, or the loads spread between the MFMAs gained nothing or
+// lost).  The 32-row tiles keep eight waves (four are no faster).
+constexpr int narrow_waves(int TM) { return TM == 64 ? 4 : 8; }
+constexpr int narrow_stages(int, bool full) { return full ? 3 : 2; }
 
 template <int TM, bool FULL>
 struct Narrow {
+  static constexpr int kKG = narrow_waves(TM);
   static constexpr int kRI = TM / 32;                       // row blocks per wave
-  static constexpr int kThreads = 64 * kNarrowKG;
+  static constexpr int kThreads = 64 * kKG;
   static constexpr int kAPer = TM * kNarrowSK / 64;         // A floats per thread
   static constexpr int kBPer = kNarrowSK * kNarrowCols / 64;  // B floats per thread (16)
   // A is staged row-major, [row][k], B as [k][col].  Full tiles are loaded
@@ -235,18 +247,16 @@ struct Narrow {
   static constexpr int kLdB = FULL ? kNarrowCols : kNarrowCols + PAD;
   static constexpr int kLdR = kNarrowCols + PAD;
   static constexpr int kStageFloats = TM * kLdA + kNarrowSK * kLdB;
-  // Full 32-row tiles keep three stages per wave (two in flight while one is
-  // multiplied): a stage holds only 16 MFMAs per wave, too short to cover a
-  // load's latency alone.  64-row tiles keep two (three would not fit).
-  static constexpr int kStages = (FULL && TM == 32) ? 3 : 2;
+  static constexpr int kStages = narrow_stages(TM, FULL);
   static constexpr int kStageLoads = (TM * kNarrowSK + kNarrowSK * kNarrowCols) / 256;
-  static constexpr int kStagingFloats = kNarrowKG * kStages * kStageFloats;
+  static constexpr int kStagingFloats = kKG * kStages * kStageFloats;
   static_assert(kStageLoads * 256 == TM * kNarrowSK + kNarrowSK * kNarrowCols, "whole loads");
-  static constexpr int kRedFloats = kNarrowKG * TM * kLdR;  // the waves' sums, over the staging
+  static constexpr int kRedFloats = kKG * TM * kLdR;  // the waves' sums, over the staging
   static constexpr int kSmemFloats = kStagingFloats > kRedFloats ? kStagingFloats : kRedFloats;
   static_assert(TM == 32 || TM == 64, "tile rows");
   static_assert(kAPer % 4 == 0 && kBPer % 4 == 0, "16-byte staging");
   static_assert(!FULL || (kLdA == 16 && kLdB == 64), "direct loads fill unpadded 1 KiB blocks");
+  static_assert(FULL ? kStages == 3 : kStages == 2, "the K loops below");
   static_assert(kSmemFloats * 4 <= 160 * 1024, "LDS of one CU");
 };
 
@@ -287,9 +297,9 @@ __device__ __forceinline__ bool narrow_col_ok(const GemmParams& P, int64_t n0, i
 }
 
 template <int MODE, int TM, bool FULL>
-__global__ __launch_bounds__(64 * kNarrowKG) void narrow_kernel(const GemmParams P) {
+__global__ __launch_bounds__(64 * narrow_waves(TM)) void narrow_kernel(const GemmParams P) {
   using G = Narrow<TM, FULL>;
-  constexpr int SK = kNarrowSK, KG = kNarrowKG, RI = G::kRI;
+  constexpr int SK = kNarrowSK, KG = G::kKG, RI = G::kRI;
   __shared__ __align__(16) float smem[G::kSmemFloats];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -439,19 +449,10 @@ __global__ __launch_bounds__(64 * kNarrowKG) void narrow_kernel(const GemmParams
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][s], b[j], acc[i][j], 0, 0, 0);
     }
   };
-  // Full tiles: the direct loads of the next stage into nxt (when issue), then
-  // the MFMAs of the stage at cur.  The restrict qualifiers state that the two
-  // stages do not overlap, so the compiler reads cur without first waiting for
-  // the loads into nxt; wait_stage() after the stage makes them visible.
-  auto full_stage = [&](const float* __restrict__ cur, float* __restrict__ nxt, bool issue) {
-    if (issue) issue_direct(nxt);
-    mfma_stage(cur);
-  };
-
   // Each wave stages and reads only its own buffers, so the K loop needs no
   // workgroup barrier: a wave's LDS accesses take effect in its issue order,
   // and its direct loads are waited for (vmcnt) before it reads them.
-  if constexpr (FULL && G::kStages == 3) {
+  if constexpr (FULL) {
     // Three stages b0, b1, b2 in rotation; stage it is multiplied from
     // buffer it % 3 while stages it + 1 and it + 2 load.  One function with
     // three restrict pointers, so that the compiler sees that reading one
@@ -478,14 +479,6 @@ __global__ __launch_bounds__(64 * kNarrowKG) void narrow_kernel(const GemmParams
       }
     };
     pipeline(stage_at(0), stage_at(1), stage_at(2));
-  } else if constexpr (FULL) {
-    issue_direct(stage_at(0));
-    wait_stage();
-    for (int it = 0; it < iters; ++it) {
-      const int buf = it & 1;
-      full_stage(stage_at(buf), stage_at(buf ^ 1), it + 1 < iters);
-      wait_stage();
-    }
   } else {
     load_checked(kt0);
     store_stage(stage_at(0));
@@ -663,7 +656,7 @@ sr_status launch_narrow(const GemmParams& P, hipStream_t stream, bool check_only
   const auto al16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
   const bool full = P.K > 0 && P.M % tm == 0 &&
                     (MODE == kPlain ? P.N % kNarrowCols == 0 : P.D_h % (kNarrowCols / 2) == 0) &&
-                    P.K % (int64_t(kNarrowSK) * kNarrowKG) == 0 && P.lda % 4 == 0 &&
+                    P.K % (int64_t(kNarrowSK) * narrow_waves(tm)) == 0 && P.lda % 4 == 0 &&
                     P.ldb % 4 == 0 && al16(P.A) && al16(P.Bm);
   if (tm == 64)
     launch_narrow_tm<MODE, 64>(full, uint32_t(tiles), P, stream);
