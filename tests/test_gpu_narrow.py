@@ -31,6 +31,13 @@ def _weights(rng, D_in, D_h, D_out):
     (64, 2048, 64, 48),       # a long K over few tiles
     (1000, 700, 333, 129),    # above 512 rows (K <= 1024): ragged rows, odd D_h
     (2048, 512, 512, 512),    # above 512 rows, every tile full
+    # 64-row tiles split K over four waves, three stage buffers each: K giving
+    # each wave one, two and three stages (the pipeline's short paths), and a
+    # ragged K that leaves waves partial or empty shares
+    (256, 64, 2048, 64),
+    (256, 128, 2048, 64),
+    (256, 192, 2048, 64),
+    (256, 100, 2048, 64),
 ])
 def test_narrow_step_matches_oracle(B, D_in, D_h, D_out):
     say(f"narrow step B={B} D_in={D_in} D_h={D_h} D_out={D_out}")
