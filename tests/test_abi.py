@@ -294,3 +294,28 @@ def test_no_alloc_scan_validates_before_any_hip_call():
                                    None) == sr.SR_ERR_INVALID_ARGUMENT   # k missing
     assert lib.mingru_scan_noalloc(2, 4, 8, FAKE, FAKE2, 8, 7, None, FAKE, None,
                                    None) == sr.SR_ERR_INVALID_ARGUMENT   # dtype
+
+
+def test_error_text_is_per_thread():
+    """Each host thread sees its own last error: eight threads fail calls with
+    different sizes at once (ctypes releases the GIL around each call) and
+    every thread reads back the message of its own call."""
+    import threading
+
+    bad = {}
+
+    def worker(i):
+        for _ in range(300):
+            st = lib.mingru_scan_noalloc(-(i + 1), 4, 4, FAKE, FAKE2, 4, sr.SR_F32, None, FAKE,
+                                         None, None)
+            msg = lib.scanrnn_last_error().decode()
+            if st != sr.SR_ERR_INVALID_ARGUMENT or f"B={-(i + 1)} " not in msg:
+                bad[i] = (st, msg)
+                return
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not bad, bad
