@@ -176,11 +176,7 @@ void chunk_scan_kernel(const ScanParams P) {
       const float gn = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gap_l), n));
       gap_max = fmaxf(gap_max, gn);
 #pragma unroll
-      for (int c = 0; c < V; ++c) {
-        float gamma, om;
-        decay_factors(nrate[c] * gn, gamma, om);
-        st[c] = Op::decayed(st[c], gamma, om);
-      }
+      for (int c = 0; c < V; ++c) st[c] = Op::decay(st[c], nrate[c] * gn);
     }
 #pragma unroll
     for (int c = 0; c < V; ++c) e[n][c] = Op::step_map(st[c]);
@@ -401,9 +397,9 @@ sr_status launch_scan(const ScanRequest& rq) {
   if (rq.op == ScanOp::kMinMax)
     err = launch_op<MinMaxOp, float>(g.V, P, rq.stream);
   else if (decay && rq.in_dtype == SR_BF16)
-    err = launch_op<MinGRUOp, uint16_t, true>(g.V, P, rq.stream);
+    err = launch_op<MinGRUDecayOp, uint16_t, true>(g.V, P, rq.stream);
   else if (decay)
-    err = launch_op<MinGRUOp, float, true>(g.V, P, rq.stream);
+    err = launch_op<MinGRUDecayOp, float, true>(g.V, P, rq.stream);
   else if (rq.in_dtype == SR_BF16)
     err = launch_op<MinGRUOp, uint16_t>(g.V, P, rq.stream);
   else

@@ -119,6 +119,60 @@ __device__ __forceinline__ void decay_factors(float nx2, float& gamma, float& om
   om = nx2 > kYSmall ? q * nx2 : 1.0f - gamma;
 }
 
+// The scan over time-decayed steps (the decayed forward scan).  A step's
+// coefficient is a gamma, gamma = 2^y with y = -x log2(e) <= 0 its decay; as
+// decay factors multiply, a composed run keeps its gates' part and its decay
+// part apart: (a, c = 1 - a) of the gates exactly as MinGRUOp composes them,
+// and y, the sum of its steps' y (non-positive terms: no cancellation).  Its
+// coefficient is a 2^y and its complement c + a (1 - 2^y), a sum of
+// non-negative terms, both accurate and formed once per composed run
+// (decay_factors on the run's y) instead of once per step.  With every y
+// zero the results are those of MinGRUOp, bit for bit.
+struct AffineDecay {
+  float a, c, y, b;
+};
+struct DecayedStep {
+  float a, c, y, full, b;  // full = a 2^y, the step's whole coefficient
+};
+
+struct MinGRUDecayOp {
+  using Step = DecayedStep;
+  using Agg = AffineDecay;
+  static __device__ __forceinline__ Agg identity() { return {1.0f, 0.0f, 0.0f, 0.0f}; }
+  // The gates' coefficient alone, the accurate one of a and 1 - c.
+  static __device__ __forceinline__ float gate_coef(Agg f) { return f.c < 0.5f ? 1.0f - f.c : f.a; }
+  // The whole coefficient: 1 - C while C < 1/2, else a 2^y.
+  static __device__ __forceinline__ float coef(Agg f) {
+    float gamma, om;
+    decay_factors(f.y, gamma, om);
+    const float fa = gate_coef(f);
+    const float C = fmaf(fa, om, f.c);
+    return C < 0.5f ? 1.0f - C : fa * gamma;
+  }
+  static __device__ __forceinline__ Agg push(Agg f, Step s) {
+    return {f.a * s.a, fmaf(f.a, s.c, f.c), f.y + s.y, fmaf(s.full, f.b, s.b)};
+  }
+  static __device__ __forceinline__ Agg compose(Agg f, Agg s) {
+    const float fa = gate_coef(f), sa = gate_coef(s);
+    return {fa * sa, fmaf(fa, s.c, f.c), f.y + s.y, fmaf(coef(s), f.b, s.b)};
+  }
+  static __device__ __forceinline__ Pair map(Agg f) { return {coef(f), f.b}; }
+  static __device__ __forceinline__ Pair step_map(Step s) { return {s.full, s.b}; }
+  static __device__ __forceinline__ float apply(Pair m, float h) { return fmaf(m.u, h, m.v); }
+  static __device__ __forceinline__ Step element(float k, float p) {
+    const Affine e = MinGRUOp::element(k, p);
+    return {e.a, e.c, 0.0f, e.a, e.b};
+  }
+  // The step with its decay y = -x log2(e) applied to the carried state.
+  static __device__ __forceinline__ Step decay(Step s, float y) {
+    return {s.a, s.c, y, s.a * __builtin_amdgcn_exp2f(y), s.b};
+  }
+  static __device__ __forceinline__ uint32_t gate_floor(Step s, uint32_t lo) {
+    return MinGRUOp::gate_floor(Affine{s.a, s.c, s.b}, lo);
+  }
+  static constexpr bool kHasGateRange = true;
+};
+
 struct MinMaxOp {
   using Step = Pair;
   using Agg = Pair;
