@@ -238,3 +238,44 @@ def test_decayed_step_over_many_streams():
         say("log1p", log1p, "error", err)
         assert err < TOL_F32
         assert int(sat.item()) == int(decay.saturated(lam, dt, log1p))
+
+
+def test_long_memory_with_small_decays_closed_form():
+    """Constant gates that keep almost all of the state (z from 6e-6 to 2.5e-3)
+    and constant small decays (x = rate * gap from 1e-6 to 1e-4), over 65536
+    steps crossing hundreds of tiles: each step's coefficient A = sigma(-k)
+    e^{-x} lies within 1e-3 of 1, and the result has the geometric closed
+    form h_t = A^t h0 + b (1 - A^t) / (1 - A), b = sigma(k) g(p), evaluated
+    in fp64 from the same fp32 inputs.  The complement 1 - A must stay
+    accurate through every composition (a cancelling 1 - e^{-x} would be off
+    by ~1e-3 relative here)."""
+    B, T, D = 2, 65536, 256
+    say(f"decayed long memory closed form B={B} T={T} D={D}")
+    rng = np.random.default_rng(1207)
+    k_ch = rng.uniform(-12.0, -6.0, (B, D)).astype(np.float32)
+    p_ch = rng.uniform(0.2, 2.0, (B, D)).astype(np.float32)
+    lam = (10.0 ** rng.uniform(-6.0, -4.0, D)).astype(np.float32)
+    gap = np.float32(1.0)
+    h0 = rng.uniform(0.5, 2.0, (B, D)).astype(np.float32)
+    k = np.broadcast_to(k_ch[:, None, :], (B, T, D))
+    p = np.broadcast_to(p_ch[:, None, :], (B, T, D))
+    dt = np.full((B, T), gap, np.float32)
+    h = sr.mingru_forward_decayed(k=dev(k), p=dev(p), h0=dev(h0), decay_rate=dev(lam),
+                                  delta_t=dev(dt))
+    torch.cuda.synchronize()
+    # closed form in fp64 (A, b as functions of the fp32 inputs)
+    k64, p64, x = k_ch.astype(np.float64), p_ch.astype(np.float64), lam.astype(np.float64) * 1.0
+    z = 1.0 / (1.0 + np.exp(-k64))
+    a = 1.0 / (1.0 + np.exp(k64))
+    log_A = -np.log1p(np.exp(k64)) - x[None, :]          # log(sigma(-k)) - x
+    one_minus_A = -np.expm1(log_A)
+    bstep = z * (p64 + 0.5)
+    ts = np.array([1, 2, 100, 1000, 10000, 30000, 65536])
+    got = host64(h)[:, ts - 1, :]
+    At = np.exp(ts[None, :, None] * log_A[:, None, :])
+    carry = At * h0.astype(np.float64)[:, None, :]
+    inp = bstep[:, None, :] * (-np.expm1(ts[None, :, None] * log_A[:, None, :])) / one_minus_A[:, None, :]
+    ref = carry + inp
+    err = float(np.max(np.abs(got - ref) / (np.abs(carry) + np.abs(inp))))
+    say("max conditioned error", err, "A^T range", float(At[..., -1].min()), float(At[..., -1].max()))
+    assert err < TOL_F32
