@@ -321,8 +321,10 @@ def leg_scan_decay(torch, sr, synth, steps, warmup):
     alg = n * 8 + B * T * 4 + D * 4 + 2 * B * D * 4
     res = launch_stats(per, alg, dict(B=B, T=T, D=D, elements_per_s=n / (wall / steps),
                                       saturated=int(sat.item())))
+    # No empty_cache() here: the headline runs next, its buffers already
+    # made, and handing gigabytes back to the driver would leave the GPU idle
+    # for milliseconds right before its warm-up.
     del kb, pb, y, ws
-    torch.cuda.empty_cache()
     return res
 
 
