@@ -613,6 +613,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     legs = [s.strip() for s in args.legs.split(",") if s.strip()]
+    # The runtime loads a kernel's code on its first use (milliseconds each):
+    # use the checks' kernels once now, not between two timed legs.
+    all_finite(torch, torch.zeros(64, device="cuda"))
     out = {"metric": METRIC}
     extra = {}
     head = None
