@@ -299,26 +299,38 @@ def leg_scan_backward(torch, sr, synth, steps, warmup):
     alg = n * 20 + 3 * B * D * 4
     res = launch_stats(per, alg, dict(B=B, T=T, D=D, elements_per_s=n / (wall / steps)))
     del kb, pb, h, dh, ws
-    torch.cuda.empty_cache()
     return res
 
 
-def leg_scan_decay(torch, sr, synth, steps, warmup):
+def prepare_scan_decay(torch, sr, synth):
+    """The decayed scan's inputs, output and workspace, made ahead (as for
+    the headline)."""
+    cfg = synth.CONFIGS[synth.SCAN]
+    B, T, D = cfg["B"], cfg["T"], cfg["D"]
+    log(f"[bench] decayed scan B={B} T={T} D={D}: generating inputs")
+    prep = dict(B=B, T=T, D=D)
+    prep["kb"] = synth.device_normal(synth.SCAN, "k", (B, T, D), cfg["k_mean"], cfg["k_std"],
+                                     torch.bfloat16)
+    prep["pb"] = synth.device_normal(synth.SCAN, "p", (B, T, D), cfg["p_mean"], cfg["p_std"],
+                                     torch.bfloat16)
+    prep["h0"] = synth.device_normal(synth.SCAN, "h0", (B, D))
+    prep["rate"] = torch.from_numpy(synth.decay_rates(synth.SCAN, D)).cuda()
+    prep["gap"] = torch.from_numpy(synth.gaps(synth.SCAN, B, T)).cuda()
+    prep["sat"] = torch.zeros(1, dtype=torch.int32, device="cuda")
+    prep["y"] = torch.empty((B, T, D), dtype=torch.float32, device="cuda")
+    prep["ws"] = torch.empty(sr.raw_library().mingru_forward_workspace_size(B, T, 0, D, D, 0, 0),
+                             dtype=torch.uint8, device="cuda")
+    return prep
+
+
+def leg_scan_decay(torch, sr, synth, steps, warmup, prep):
     """The headline scan shape with time decay of the carried state: k, p
     (bf16) in, h (fp32) out as in the plain scan, plus one gap per (b, t) and
     one rate per channel: 8 + 4/D algorithmic bytes per element."""
-    cfg = synth.CONFIGS[synth.SCAN]
-    B, T, D = cfg["B"], cfg["T"], cfg["D"]
+    B, T, D = prep["B"], prep["T"], prep["D"]
+    kb, pb, h0, rate, gap, sat, y, ws = (prep[k] for k in
+                                        ("kb", "pb", "h0", "rate", "gap", "sat", "y", "ws"))
     log(f"[bench] decayed scan B={B} T={T} D={D}")
-    kb = synth.device_normal(synth.SCAN, "k", (B, T, D), cfg["k_mean"], cfg["k_std"], torch.bfloat16)
-    pb = synth.device_normal(synth.SCAN, "p", (B, T, D), cfg["p_mean"], cfg["p_std"], torch.bfloat16)
-    h0 = synth.device_normal(synth.SCAN, "h0", (B, D))
-    rate = torch.from_numpy(synth.decay_rates(synth.SCAN, D)).cuda()
-    gap = torch.from_numpy(synth.gaps(synth.SCAN, B, T)).cuda()
-    sat = torch.zeros(1, dtype=torch.int32, device="cuda")
-    y = torch.empty((B, T, D), dtype=torch.float32, device="cuda")
-    ws = torch.empty(sr.raw_library().mingru_forward_workspace_size(B, T, 0, D, D, 0, 0),
-                     dtype=torch.uint8, device="cuda")
     wall, per = time_launches(
         torch, lambda: sr.mingru_forward_decayed(k=kb, p=pb, h0=h0, decay_rate=rate, delta_t=gap,
                                                  saturated=sat, workspace=ws, out=y),
@@ -333,6 +345,7 @@ def leg_scan_decay(torch, sr, synth, steps, warmup):
     # made, and handing gigabytes back to the driver would leave the GPU idle
     # for milliseconds right before its warm-up.
     del kb, pb, y, ws
+    prep.clear()
     return res
 
 
@@ -362,7 +375,6 @@ def leg_scan_backward_decay(torch, sr, synth, steps, warmup):
     alg = n * 20 + B * T * 4 + D * 4 + 3 * B * D * 4
     res = launch_stats(per, alg, dict(B=B, T=T, D=D, elements_per_s=n / (wall / steps)))
     del kb, pb, h, dh, ws
-    torch.cuda.empty_cache()
     return res
 
 
@@ -507,7 +519,6 @@ def leg_copy(torch):
     copy_ms = median(time_launches(torch, lambda: b.copy_(a), 40, 3)[1])
     elem_ms = median(time_launches(torch, lambda: torch.neg(a, out=b), 40, 3)[1])
     del a, b
-    torch.cuda.empty_cache()
     nbytes = 2 * 4 * n
     copy_gbps, elem_gbps = nbytes / (copy_ms * 1e-3) / 1e9, nbytes / (elem_ms * 1e-3) / 1e9
     return dict(bytes_per_copy=nbytes, GBps=max(copy_gbps, elem_gbps), device_copy_GBps=copy_gbps,
@@ -614,8 +625,16 @@ def main():
         sys.exit(1)
     legs = [s.strip() for s in args.legs.split(",") if s.strip()]
     # The runtime loads a kernel's code on its first use (milliseconds each):
-    # use the checks' kernels once now, not between two timed legs.
+    # use the checks' kernels and the full-size scans' kernel variants once
+    # now, on small inputs, not between two timed legs (an idle stretch
+    # before a leg makes its first launches' clocks overshoot and dip).
     all_finite(torch, torch.zeros(64, device="cuda"))
+    kw = torch.zeros((1, 300, 256), dtype=torch.bfloat16, device="cuda")
+    hw = torch.zeros((1, 256), device="cuda")
+    sr.mingru_forward(k=kw, p=kw, h0=hw)
+    sr.mingru_forward_decayed(k=kw, p=kw, h0=hw, decay_rate=torch.zeros(256, device="cuda"),
+                              delta_t=torch.zeros((1, 300), device="cuda"))
+    torch.cuda.synchronize()
     out = {"metric": METRIC}
     extra = {}
     head = None
@@ -623,11 +642,12 @@ def main():
     # ceiling just before it), so that it is timed on a GPU already at its
     # sustained clock rather than in the first milliseconds of the process.
     # Order: the short and launch-bound legs first, then the copy ceiling,
-    # then the full-size scans, the headline last.  The headline's inputs are
-    # made before the time-decayed scan, so that the decayed scan's
-    # sustained, VALU- and HBM-heavy launches run right before the headline's
-    # warm-up (after a lighter leg such as a copy the clocks take some ten
-    # launches to return, and the first launches run 5-10% slower).
+    # then the full-size scans, the headline last.  The inputs of the last
+    # two legs (decayed scan, headline) are made before the backward legs,
+    # so that no allocation or host-side generation leaves the GPU idle
+    # between those timed legs: after an idle stretch of some milliseconds a
+    # leg's launches run up to 15% slower for about ten launches (the clocks
+    # overshoot and recover).
     if "minmax" in legs:
         extra["minmax_b8_t32768_d192"] = leg_minmax(torch, sr, synth, args.steps, args.warmup)
     if "minmax_bwd" in legs:
@@ -647,14 +667,16 @@ def main():
         extra["stream_ceilings"] = leg_streams(torch)
     if "copy" in legs:
         extra["copy_ceiling"] = leg_copy(torch)
+    prep = prepare_scan(torch, sr, synth) if "scan" in legs else None
+    prep_decay = prepare_scan_decay(torch, sr, synth) if "scan_decay" in legs else None
     if "scan_bwd" in legs:
         extra["backward_b8_t65536_d1024"] = leg_scan_backward(torch, sr, synth, args.steps, args.warmup)
     if "scan_decay_bwd" in legs:
         extra["decayed_backward_b8_t65536_d1024"] = leg_scan_backward_decay(
             torch, sr, synth, args.steps, args.warmup)
-    prep = prepare_scan(torch, sr, synth) if "scan" in legs else None
     if "scan_decay" in legs:
-        extra["decayed_b8_t65536_d1024"] = leg_scan_decay(torch, sr, synth, args.steps, args.warmup)
+        extra["decayed_b8_t65536_d1024"] = leg_scan_decay(torch, sr, synth, args.steps, args.warmup,
+                                                          prep_decay)
     if "scan" in legs:
         head = leg_scan(torch, sr, synth, args.steps, args.warmup, args.cpu_steps, prep)
     if head is not None:
