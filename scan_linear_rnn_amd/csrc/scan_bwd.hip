@@ -30,6 +30,8 @@
 // only if strictly greater than min(r, x), r only if strictly smaller than x;
 // otherwise the state passes.
 
+#include <type_traits>
+
 #include "scan_engine.hpp"
 
 namespace sr {
@@ -90,10 +92,14 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(kBwdWave
 void scan_backward_kernel(const BwdParams Q) {
   using R = Raw<TIn, V>;
   using RF = Raw<float, V>;
+  // The reverse maps G -> coef G + grad compose as the forward's do; with
+  // time decay their runs keep the gates' part and the summed log2 decay
+  // apart (MinGRUDecayOp), so each step's decay needs no complement.
+  using Op = std::conditional_t<KIND == kMinGRU && kDecay, MinGRUDecayOp, MinGRUOp>;
   constexpr int Dc = 64 * V;
   const ScanParams& P = Q.core;
   __shared__ uint32_t s_ticket;
-  __shared__ Affine s_pre[W][Dc];
+  __shared__ typename Op::Agg s_pre[W][Dc];
   __shared__ uint64_t s_win[kWindowTiles][Dc];
   __shared__ float s_hin[Dc];
 
@@ -172,18 +178,36 @@ void scan_backward_kernel(const BwdParams Q) {
     for (int c = 0; c < V; ++c) nrate[c] = rv[c] * kNegLog2e;
     if (Q.log1p_gap) gap_l = log1pf(gap_l);  // after the input loads are issued
   }
-  // The decay factor of step (t_hi + 1 - i) for each of the lane's channels,
-  // and its complement 1 - gamma.
-  auto decay_at = [&](int i, float (&gam)[V], float (&om)[V]) {
+  // The log2 decay y and the factor gamma = 2^y of time t_hi + 1 - i (i = 0
+  // .. N) for each of the lane's channels, formed once here: phase 1 and
+  // phase 3 both use them.
+  constexpr int ND = kDecay ? N + 1 : 1;
+  float ylog[ND][V], gamma_at[ND][V];
+  if constexpr (kDecay) {
+#pragma unroll
+    for (int i = 0; i <= N; ++i) {
+      const float gp = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gap_l), i));
+#pragma unroll
+      for (int c = 0; c < V; ++c) {
+        ylog[i][c] = nrate[c] * gp;
+        gamma_at[i][c] = __builtin_amdgcn_exp2f(ylog[i][c]);
+      }
+    }
+  }
+  // The decay factor and log2 decay of step (t_hi + 1 - i) for each of the
+  // lane's channels (the plain scan: 1 and 0).
+  auto decay_at = [&](int i, float (&gam)[V], float (&y)[V]) {
 #pragma unroll
     for (int c = 0; c < V; ++c) {
       gam[c] = 1.0f;
-      om[c] = 0.0f;
+      y[c] = 0.0f;
     }
     if constexpr (kDecay) {
-      const float gp = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gap_l), i));
 #pragma unroll
-      for (int c = 0; c < V; ++c) decay_factors(nrate[c] * gp, gam[c], om[c]);
+      for (int c = 0; c < V; ++c) {
+        gam[c] = gamma_at[i][c];
+        y[c] = ylog[i][c];
+      }
     }
   };
 
@@ -199,15 +223,19 @@ void scan_backward_kernel(const BwdParams Q) {
   // for t = T - 1, where the gradient on the returned final state enters.
   auto step_coef = [&](int n, float (&coef)[V], float (&comp)[V]) {
     if (KIND == kMinGRU) {
-      float kn[V], gam[V], om[V];
+      float kn[V], gam[V], yv[V];
       R::unpack(i0[n], kn);  // k_{t+1}
-      decay_at(n, gam, om);  // gamma_{t+1}
+      decay_at(n, gam, yv);  // gamma_{t+1}
 #pragma unroll
       for (int c = 0; c < V; ++c) {
-        float z, a;
+        float z, a, om = 0.0f;
         sig_pair(kn[c], z, a);
+        if constexpr (kDecay) {
+          float unused;
+          decay_factors(yv[c], unused, om);
+        }
         coef[c] = a * gam[c];
-        comp[c] = fmaf(a, om[c], z);  // 1 - a gamma = z + a (1 - gamma)
+        comp[c] = fmaf(a, om, z);  // 1 - a gamma = z + a (1 - gamma)
       }
     } else {
       float rn[V], sn[V], xn[V];
@@ -233,23 +261,45 @@ void scan_backward_kernel(const BwdParams Q) {
   // their complements 1 - coef (see Affine).  The maps are not kept: phase 3
   // gets each step's coefficient as the one it forms for the step before
   // (bit for bit the same arithmetic), and the gradient is still loaded.
-  Affine agg[V];
+  typename Op::Agg agg[V];
 #pragma unroll
-  for (int c = 0; c < V; ++c) agg[c] = MinGRUOp::identity();
+  for (int c = 0; c < V; ++c) agg[c] = Op::identity();
 #pragma unroll
   for (int n = 0; n < N; ++n) {
-    float gv[V], coef[V], comp[V];
+    float gv[V];
     RF::unpack(gr[n], gv);
-    step_coef(n, coef, comp);
-    if (n < nvalid) {
+    if constexpr (KIND == kMinGRU && kDecay) {
+      // Step n's map: the gates' part of the following step (a, z), its
+      // log2 decay y, and its whole coefficient a 2^y, formed as step_coef
+      // forms it (phase 3 replays with that one); identity gates and no
+      // decay at t = T - 1.
+      float kn[V];
+      R::unpack(i0[n], kn);  // k_{t+1}
+      const bool last = t_hi - n == T - 1;
+      if (n < nvalid) {
 #pragma unroll
-      for (int c = 0; c < V; ++c) agg[c] = MinGRUOp::push(agg[c], Affine{coef[c], comp[c], gv[c]});
+        for (int c = 0; c < V; ++c) {
+          float z, a;
+          sig_pair(kn[c], z, a);
+          const DecayedStep st =
+              last ? DecayedStep{1.0f, 0.0f, 0.0f, 1.0f, gv[c]}
+                   : DecayedStep{a, z, ylog[n][c], a * gamma_at[n][c], gv[c]};
+          agg[c] = Op::push(agg[c], st);
+        }
+      }
+    } else {
+      float coef[V], comp[V];
+      step_coef(n, coef, comp);
+      if (n < nvalid) {
+#pragma unroll
+        for (int c = 0; c < V; ++c) agg[c] = Op::push(agg[c], Affine{coef[c], comp[c], gv[c]});
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
   }
   if (!lane_on) {
 #pragma unroll
-    for (int c = 0; c < V; ++c) agg[c] = MinGRUOp::identity();
+    for (int c = 0; c < V; ++c) agg[c] = Op::identity();
   }
 #pragma unroll
   for (int c = 0; c < V; ++c) s_pre[wave][lane * V + c] = agg[c];
@@ -257,7 +307,7 @@ void scan_backward_kernel(const BwdParams Q) {
 
   // Phase 2: the gradient entering the tile (decoupled look-back), its
   // fallback walking SB words per round trip (chosen per launch).
-  resolve_tile<MinGRUOp, W, Dc, 64 * W, SB>(P, tl, s_pre, s_win, s_hin);
+  resolve_tile<Op, W, Dc, 64 * W, SB>(P, tl, s_pre, s_win, s_hin);
 
   // Phase 3: replay to get G at every step and form the input gradients.
   // coef_next: the coefficient of the next step's map (the first from the
@@ -265,7 +315,7 @@ void scan_backward_kernel(const BwdParams Q) {
   float G[V], coef_next[V];
 #pragma unroll
   for (int c = 0; c < V; ++c)
-    G[c] = MinGRUOp::apply(MinGRUOp::map(s_pre[wave][lane * V + c]), s_hin[lane * V + c]);
+    G[c] = Op::apply(Op::map(s_pre[wave][lane * V + c]), s_hin[lane * V + c]);
   {
     float comp0[V];
     step_coef(0, coef_next, comp0);
@@ -284,11 +334,11 @@ void scan_backward_kernel(const BwdParams Q) {
     }
     float o0v[V], o1v[V], pass_or_a[V];
     if (KIND == kMinGRU) {
-      float kt[V], pt[V], hp[V], gam[V], om[V];
+      float kt[V], pt[V], hp[V], gam[V], yv[V];
       R::unpack(i0[n + 1], kt);
       R::unpack(i1[n], pt);
       RF::unpack(fw[n], hp);
-      decay_at(n + 1, gam, om);  // gamma_t
+      decay_at(n + 1, gam, yv);  // gamma_t
 #pragma unroll
       for (int c = 0; c < V; ++c) {
         const float h_prev = (t == 0 ? init_state[c] : hp[c]) * gam[c];
