@@ -98,6 +98,20 @@ def time_launches(torch, fn, steps, warmup):
     return wall, [s.elapsed_time(e) for s, e in zip(starts, ends)]
 
 
+def release_cached(torch):
+    """Hands the blocks freed by earlier legs back to the driver, so that a
+    leg's large tensors are fresh allocations, as in a process of its own.
+    The backward reads four and writes two tensors of 1-2 GiB at the same
+    offsets; how their base addresses fall relative to each other moves its
+    time by up to ~9% (the same kernel: 1.77 ms with the six carved from one
+    buffer at GiB boundaries, 1.93 ms with each shifted by a further 6 MiB),
+    and blocks reused from earlier legs of other shapes had cost the decayed
+    backward 13% (2.107 vs 1.867 ms in one process).  Called before a leg
+    makes its inputs, so the GPU is busy again (inputs, forward pass,
+    warm-up) before its timed launches."""
+    torch.cuda.empty_cache()
+
+
 def all_finite(torch, t):
     """Whether every element of t is finite, from its minimum and maximum
     (NaN and infinities reach them): two reductions, no temporaries of t's
@@ -286,6 +300,7 @@ def leg_scan_backward(torch, sr, synth, steps, warmup):
     cfg = synth.CONFIGS[synth.SCAN]
     B, T, D = cfg["B"], cfg["T"], cfg["D"]
     log(f"[bench] scan backward B={B} T={T} D={D}")
+    release_cached(torch)
     kb = synth.device_normal(synth.SCAN, "k", (B, T, D), cfg["k_mean"], cfg["k_std"], torch.bfloat16)
     pb = synth.device_normal(synth.SCAN, "p", (B, T, D), cfg["p_mean"], cfg["p_std"], torch.bfloat16)
     h0 = synth.device_normal(synth.SCAN, "h0", (B, D))
@@ -356,6 +371,7 @@ def leg_scan_backward_decay(torch, sr, synth, steps, warmup):
     cfg = synth.CONFIGS[synth.SCAN]
     B, T, D = cfg["B"], cfg["T"], cfg["D"]
     log(f"[bench] decayed scan backward B={B} T={T} D={D}")
+    release_cached(torch)
     kb = synth.device_normal(synth.SCAN, "k", (B, T, D), cfg["k_mean"], cfg["k_std"], torch.bfloat16)
     pb = synth.device_normal(synth.SCAN, "p", (B, T, D), cfg["p_mean"], cfg["p_std"], torch.bfloat16)
     h0 = synth.device_normal(synth.SCAN, "h0", (B, D))
