@@ -400,6 +400,7 @@ def leg_minmax_backward(torch, sr, synth, steps, warmup):
     cfg = synth.CONFIGS[synth.MINMAX]
     B, T, D = cfg["B"], cfg["T"], cfg["D"]
     log(f"[bench] minmax backward B={B} T={T} D={D}")
+    release_cached(torch)
     r = synth.device_uniform(synth.MINMAX, "r", (B, T, D), -1.0, 1.0)
     s = synth.device_uniform(synth.MINMAX, "s", (B, T, D), -1.5, 0.5)
     x0 = synth.device_uniform(synth.MINMAX, "x0", (B, D), -1.0, 1.0)
