@@ -99,7 +99,7 @@ def time_launches(torch, fn, steps, warmup):
 
 
 def release_cached(torch):
-    """Hands the blocks freed by earlier legs back to the driver, so that a
+    """Hands the blocks freed by earlier legs back to the HIP runtime, so that a
     leg's large tensors are fresh allocations, as in a process of its own.
     The backward reads four and writes two tensors of 1-2 GiB at the same
     offsets; how their base addresses fall relative to each other moves its
@@ -357,7 +357,7 @@ def leg_scan_decay(torch, sr, synth, steps, warmup, prep):
     res = launch_stats(per, alg, dict(B=B, T=T, D=D, elements_per_s=n / (wall / steps),
                                       saturated=int(sat.item())))
     # No empty_cache() here: the headline runs next, its buffers already
-    # made, and handing gigabytes back to the driver would leave the GPU idle
+    # made, and handing gigabytes back to the HIP runtime would leave the GPU idle
     # for milliseconds right before its warm-up.
     del kb, pb, y, ws
     prep.clear()
