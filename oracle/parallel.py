@@ -83,8 +83,20 @@ def map_slices(task, arrays: dict, slices, workers: int | None = None, timeout: 
             specs[name] = (shm.name, a.shape, a.dtype.str)
         ctx = mp.get_context("spawn")
         jobs = [(task.__module__, task.__name__, sl) for sl in slices]
-        with ctx.Pool(workers, initializer=_attach, initargs=(specs,)) as pool:
-            return pool.map_async(_run, jobs, chunksize=1).get(timeout)
+        pool = ctx.Pool(workers, initializer=_attach, initargs=(specs,))
+        try:
+            out = pool.map_async(_run, jobs, chunksize=1).get(timeout)
+        except BaseException:
+            pool.terminate()
+            pool.join()
+            raise
+        # The workers are let finish and exit on their own rather than being
+        # sent SIGTERM (what leaving a `with Pool` block does): a process
+        # tool preloaded into them (a profiler) may not survive that signal
+        # cleanly, and the parent would then wait for them forever.
+        pool.close()
+        pool.join()
+        return out
     finally:
         for shm in shms:
             shm.close()
