@@ -35,7 +35,9 @@ carries:
                 Opt-in (name them in --legs): shapes -- one scan call over
                 the sweep shapes (both operators, bf16 and fp32 inputs);
                 streams -- read-only, write-only and read+write ceilings of
-                torch's own kernels on 2 GiB.
+                torch's own kernels on 2 GiB; placement -- the full-size
+                backward (plain and decayed) and forward with their large
+                tensors carved from one buffer at chosen relative offsets.
 
 The headline scan is measured last, after the other legs, on a GPU already
 at its sustained clock: the full-size backward and time-decayed scans run
@@ -592,6 +594,76 @@ def leg_shapes(torch, sr, synth, steps, warmup):
     return res
 
 
+# Relative placements of the placement leg: each tensor's base moves by this
+# many bytes beyond the end of the previous one (0: bases 1-2 GiB apart).
+PLACEMENT_SHIFTS = [("packed", 0), ("each_+256B", 256), ("each_+64KiB", 64 << 10),
+                    ("each_+2MiB", 2 << 20), ("each_+6MiB", 6 << 20), ("each_+37MiB", 37 << 20)]
+
+
+def leg_placement(torch, sr, synth, steps, warmup):
+    """The config-3-shape backward (plain and decayed) and forward with their
+    six (backward) or three (forward) large tensors carved from one buffer:
+    every base moved by the same shift past the end of the previous tensor.
+    Median of the HIP events per call, through the C ABI."""
+    import ctypes
+    lib = sr.raw_library()
+    cfg = synth.CONFIGS[synth.SCAN]
+    B, T, D = cfg["B"], cfg["T"], cfg["D"]
+    n = B * T * D
+    names = ["k", "p", "h", "dh", "dk", "dp"]
+    sizes = [2 * n, 2 * n, 4 * n, 4 * n, 4 * n, 4 * n]
+    total = sum(sizes) + len(sizes) * max(s for _, s in PLACEMENT_SHIFTS) + 256
+    log(f"[bench] placement: one {total / 2**30:.1f} GiB buffer")
+    release_cached(torch)
+    buf = torch.empty(total, dtype=torch.uint8, device="cuda")
+    h0 = synth.device_normal(synth.SCAN, "h0", (B, D))
+    dh0 = torch.empty_like(h0)
+    last = torch.empty_like(h0)
+    rate = torch.from_numpy(synth.decay_rates(synth.SCAN, D)).cuda()
+    gap = torch.from_numpy(synth.gaps(synth.SCAN, B, T)).cuda()
+    wsb = lib.mingru_scan_backward_workspace_size(B, T, D)
+    wsf = lib.mingru_forward_workspace_size(B, T, 0, D, D, 0, 0)
+    ws = torch.empty(max(wsb, wsf), dtype=torch.uint8, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+
+    def check(st):
+        if st != 0:
+            raise RuntimeError(f"placement leg: status {st}: {sr.raw_library().scanrnn_last_error()}")
+
+    res = {}
+    for tag, shift in PLACEMENT_SHIFTS:
+        v, off = {}, 0
+        for nm, size in zip(names, sizes):
+            off += shift
+            v[nm] = buf[off:off + size].view(torch.bfloat16 if nm in ("k", "p") else torch.float32)
+            v[nm] = v[nm].view(B, T, D)
+            off += size
+        assert off <= total
+        v["k"].normal_(cfg["k_mean"], cfg["k_std"])
+        v["p"].normal_(cfg["p_mean"], cfg["p_std"])
+        v["dh"].normal_(0.0, 1.0)
+        fwd = lambda: check(lib.mingru_forward(B, T, 0, D, D, None, None, P(v["k"]), P(v["p"]), D, 1,
+                                               P(h0), None, P(v["h"]), P(last), P(ws), wsf, stream))
+        bwd = lambda: check(lib.mingru_scan_backward(B, T, D, P(v["k"]), P(v["p"]), D, 1, P(h0),
+                                                     P(v["h"]), P(v["dh"]), None, P(v["dk"]),
+                                                     P(v["dp"]), P(dh0), P(ws), wsb, stream))
+        dec = lambda: check(lib.mingru_scan_backward_decayed(
+            B, T, D, P(v["k"]), P(v["p"]), D, 1, P(rate), P(gap), 0, P(h0), P(v["h"]), P(v["dh"]),
+            None, P(v["dk"]), P(v["dp"]), P(dh0), P(ws), wsb, stream))
+        fwd()  # h from this layout's inputs
+        res[tag] = {
+            "shift_bytes": shift,
+            "forward_ms_median": median(time_launches(torch, fwd, steps, warmup)[1]),
+            "backward_ms_median": median(time_launches(torch, bwd, steps, warmup)[1]),
+            "decayed_backward_ms_median": median(time_launches(torch, dec, steps, warmup)[1]),
+        }
+        log(f"[bench] placement {tag}: {res[tag]}")
+    del buf, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def leg_streams(torch):
     """Streaming ceilings on 2 GiB fp32 buffers with torch's own kernels:
     read-only (a sum), write-only (a fill), read + write (copy, and an
@@ -682,6 +754,8 @@ def main():
         extra["scan_shapes"] = leg_shapes(torch, sr, synth, 20, 5)
     if "streams" in legs:
         extra["stream_ceilings"] = leg_streams(torch)
+    if "placement" in legs:
+        extra["placement_b8_t65536_d1024"] = leg_placement(torch, sr, synth, 40, 60)
     if "copy" in legs:
         extra["copy_ceiling"] = leg_copy(torch)
     prep = prepare_scan(torch, sr, synth) if "scan" in legs else None
