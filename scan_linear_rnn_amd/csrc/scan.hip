@@ -53,6 +53,8 @@
 // is exactly how tile i+1..j-1 compute their own end states; the state
 // entering tile j is therefore the same bits however far the look-back went.
 
+#include <type_traits>
+
 #include "scan_engine.hpp"
 
 namespace sr {
@@ -82,10 +84,13 @@ sr_status reset_workspace(void* ws, size_t used, hipStream_t stream) {
 namespace {
 using namespace eng;
 
-template <class Op, typename TIn, int V, bool kDecay>
+// E: maps each lane keeps (N * V); kElemsPerLane except for the MinMax
+// scan's shorter tiles (choose_geometry).
+template <class Op, typename TIn, int V, bool kDecay, int E = kElemsPerLane>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd)))
 void chunk_scan_kernel(const ScanParams P) {
-  constexpr int N = kElemsPerLane / V;
+  static_assert(E % V == 0 && E <= kElemsPerLane, "whole runs within the register budget");
+  constexpr int N = E / V;
   constexpr int W = kWaves;
   using R = Raw<TIn, V>;
   using Agg = typename Op::Agg;
@@ -260,17 +265,21 @@ __global__ void copy_or_zero_kernel(float* dst, const float* src, int64_t n) {
     dst[i] = src ? src[i] : 0.0f;
 }
 
-template <class Op, typename TIn, int V, bool kDecay>
+template <class Op, typename TIn, int V, bool kDecay, int E = kElemsPerLane>
 hipError_t launch_v(const ScanParams& P, hipStream_t stream) {
   const int64_t n_blocks = P.n_chains * P.n_tchunks;
-  hipLaunchKernelGGL((chunk_scan_kernel<Op, TIn, V, kDecay>), dim3(uint32_t(n_blocks)),
+  hipLaunchKernelGGL((chunk_scan_kernel<Op, TIn, V, kDecay, E>), dim3(uint32_t(n_blocks)),
                      dim3(64 * kWaves), 0, stream, P);
   return hipGetLastError();
 }
 
 template <class Op, typename TIn, bool kDecay = false>
-hipError_t launch_op(int V, const ScanParams& P, hipStream_t stream) {
-  return V == 2 ? launch_v<Op, TIn, 2, kDecay>(P, stream) : launch_v<Op, TIn, 1, kDecay>(P, stream);
+hipError_t launch_op(const ScanGeometry& g, const ScanParams& P, hipStream_t stream) {
+  if constexpr (std::is_same_v<Op, MinMaxOp>) {
+    if (g.V == 1 && g.N == addr::kFwdElemsPerLaneShort)
+      return launch_v<Op, TIn, 1, kDecay, addr::kFwdElemsPerLaneShort>(P, stream);
+  }
+  return g.V == 2 ? launch_v<Op, TIn, 2, kDecay>(P, stream) : launch_v<Op, TIn, 1, kDecay>(P, stream);
 }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -299,6 +308,18 @@ ScanGeometry choose_geometry(const ScanRequest& rq) {
   ScanGeometry g;
   g.V = V;
   g.N = kElemsPerLane / V;
+  // The MinMax scan with one channel per lane and at least 16 chains takes
+  // 240-step tiles (20 steps per lane) instead of 288: its maps are two
+  // selections, so a tile's work is almost all loads and stores, and the
+  // shorter tiles even out the last of the launch.  Measured (fp32, median
+  // of 50 launches after 100, one process): 8 x 32768 x 192 (24 chains)
+  // 120.7 -> 116.9 us, 32 x 32768 x 192 436.1 -> 427.6 us, 8 x 131072 x 192
+  // 418.8 -> 415.0 us; with 3 chains (1 x 262144 x 192) 153.5 -> 171.4 us
+  // and with two channels per lane (8 x 65536 x 1024) 1106 -> 1113 us, so
+  // those keep 288.
+  constexpr int64_t kShortMinChains = 16;
+  if (rq.op == ScanOp::kMinMax && V == 1 && rq.B * tiles_1 >= kShortMinChains)
+    g.N = addr::kFwdElemsPerLaneShort;
   g.W = kWaves;
   g.Dc = 64 * V;
   g.Tc = int64_t(g.W) * g.N;
@@ -395,15 +416,15 @@ sr_status launch_scan(const ScanRequest& rq) {
   hipError_t err;
   const bool decay = rq.decay_rate != nullptr;
   if (rq.op == ScanOp::kMinMax)
-    err = launch_op<MinMaxOp, float>(g.V, P, rq.stream);
+    err = launch_op<MinMaxOp, float>(g, P, rq.stream);
   else if (decay && rq.in_dtype == SR_BF16)
-    err = launch_op<MinGRUDecayOp, uint16_t, true>(g.V, P, rq.stream);
+    err = launch_op<MinGRUDecayOp, uint16_t, true>(g, P, rq.stream);
   else if (decay)
-    err = launch_op<MinGRUDecayOp, float, true>(g.V, P, rq.stream);
+    err = launch_op<MinGRUDecayOp, float, true>(g, P, rq.stream);
   else if (rq.in_dtype == SR_BF16)
-    err = launch_op<MinGRUOp, uint16_t>(g.V, P, rq.stream);
+    err = launch_op<MinGRUOp, uint16_t>(g, P, rq.stream);
   else
-    err = launch_op<MinGRUOp, float>(g.V, P, rq.stream);
+    err = launch_op<MinGRUOp, float>(g, P, rq.stream);
   if (err != hipSuccess) return fail(SR_ERR_HIP, "scan launch: %s", hipGetErrorString(err));
   return SR_OK;
 }

@@ -22,6 +22,9 @@ namespace addr {
 // T) and maps each lane keeps in registers (steps x channels per lane).
 constexpr int kFwdWaves = 12;
 constexpr int kFwdElemsPerLane = 24;
+// The MinMax scan's shorter tiles (one channel per lane, 20 steps per lane)
+// for launches with enough chains.
+constexpr int kFwdElemsPerLaneShort = 20;
 constexpr int kBwdWaves = 8;
 constexpr int kBwdElemsPerLane = 16;
 

@@ -124,7 +124,7 @@ static void check_backward(int64_t B, int64_t T, int64_t D, int64_t ld, int V, i
 
 int main() {
   // The kernels' own geometry (scan_addr.hpp).
-  const int64_t Ts[] = {1, 2, 5, 23, 24, 25, 143, 144, 145, 287, 288, 289, 300, 1000};
+  const int64_t Ts[] = {1, 2, 5, 19, 20, 21, 23, 24, 25, 143, 144, 145, 239, 240, 241, 287, 288, 289, 300, 1000};
   const int64_t Ds[] = {1, 2, 3, 16, 63, 64, 65, 127, 128, 130, 192, 200, 257};
   const int64_t Bs[] = {1, 2, 3};
   for (int64_t B : Bs)
@@ -135,6 +135,7 @@ int main() {
             const int64_t ld = D + extra;
             if (V == 2 && (D % 2 || ld % 2)) continue;
             check_forward(B, T, D, ld, V, kFwdWaves, kFwdElemsPerLane);
+            if (V == 1) check_forward(B, T, D, ld, V, kFwdWaves, kFwdElemsPerLaneShort);
             check_backward(B, T, D, ld, V, kBwdWaves, kBwdElemsPerLane);
           }
   std::printf("forward and backward addressing: %lld accesses checked, all inside their tensors\n",

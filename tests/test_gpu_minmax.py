@@ -25,6 +25,8 @@ def _inputs(B, T, D, seed):
 
 @pytest.mark.parametrize("B,T,D", [
     (2, 64, 16), (3, 1000, 200), (1, 1, 5), (2, 5000, 192), (4, 3333, 7), (1, 40000, 64),
+    # 32 chains of one channel per lane: the 240-step tiles, ragged in T and D.
+    (8, 5001, 200), (16, 241, 65),
 ])
 def test_minmax_bitwise(B, T, D):
     say(f"minmax B={B} T={T} D={D}")
