@@ -43,10 +43,14 @@ struct FusedParams {
 };
 
 // Register budget: 4 waves per SIMD (two workgroups per CU), as the plain
-// 256-row GEMM runs.  The scan epilogue then spills a few dozen registers,
-// once per tile; measured 17.3 ms against 19.1 ms at the compiler's own
+// 256-row GEMM runs; measured 17.3 ms against 19.1 ms at the compiler's own
 // choice (2 waves per SIMD) on a 131072 x 4096 x 2048 projection (B=256,
-// T=512, D=2048).
+// T=512, D=2048).  Within it the epilogue keeps the per-row maps in the
+// accumulators, the runs' entry prefixes in the K loop's staging LDS and
+// its row tests relative to the lane's first row: 121 VGPRs without decay,
+// no spills (the decayed variant spills 25 dwords once per tile).  Before,
+// 65 dwords (prefixes and 64-bit row indices) spilled and were reloaded per
+// tile, at no measurable cost (16.66 vs 16.69 ms on that projection).
 template <bool kDecay, bool kFull>
 __global__ __launch_bounds__(2 * kTileT) __attribute__((amdgpu_waves_per_eu(4)))
 void fused_proj_scan_kernel(const FusedParams F) {
@@ -68,6 +72,11 @@ void fused_proj_scan_kernel(const FusedParams F) {
   const Tile tl = decode_ticket(P, ticket, kTileD);
   const int64_t t0 = tl.tchunk * kTileT;
   const int64_t rows = P.T - t0 < kTileT ? P.T - t0 : kTileT;
+  // Row tests in the epilogue compare the row's offset within the lane's
+  // runs (a constant there) with these per-lane bounds, so that no per-row
+  // index is kept across the look-back.
+  const int row_base = wm * 64 + (lane >> 5) * 4;  // the lane's first row in the tile
+  const int rows_rel = int(rows) - row_base;      // rows [0, rows) are inside the sequence
   const int c = wn * 32 + ml;  // channel within the tile
   const int64_t d = tl.d0 + c;
   const bool chan_ok = d < P.D;
@@ -101,8 +110,9 @@ void fused_proj_scan_kernel(const FusedParams F) {
     for (int j = 0; j < 4; ++j) {
       const int r = 4 * q + j;
       const int lr = wm * 64 + i * 32 + q * 8 + kl * 4 + j;
+      const bool in_seq = i * 32 + q * 8 + j < rows_rel;  // lr < rows
       Affine m = MinGRUOp::element(acc[i][0][r], acc[i][1][r]);
-      if (lr < rows) gate_lo = MinGRUOp::gate_floor(m, gate_lo);
+      if (in_seq) gate_lo = MinGRUOp::gate_floor(m, gate_lo);
       if constexpr (kDecay) {
         const float gp = s_gap[lr];
         float gamma, om;
@@ -110,7 +120,7 @@ void fused_proj_scan_kernel(const FusedParams F) {
         m = MinGRUOp::decayed(m, gamma, om);
         sat = sat || (rate * gp > kDecayClamp);
       }
-      if (lr >= rows) m = MinGRUOp::identity();
+      if (!in_seq) m = MinGRUOp::identity();
       acc[i][0][r] = m.a;
       acc[i][1][r] = m.b;
       run_n = MinGRUOp::push(run_n, m);
@@ -125,7 +135,14 @@ void fused_proj_scan_kernel(const FusedParams F) {
     __hip_atomic_fetch_or(P.status, kStatusGateRange, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   // 2. The partner lane's runs (lane ^ 32), then the prefix over the wave's
   // 16 runs in T order: run 2n is lane kl = 0's run n, run 2n + 1 lane 1's.
-  Pair pre[8];
+  // The prefixes entering the lane's runs wait for step 4 in the staging LDS
+  // of the K loop, which is free now (in registers they would spill).
+  float* const pre = &As[0][0][0];  // [8][2][512]: run n's (u, v) of thread tid
+  static_assert(8 * 2 * 2 * kTileT <= 2 * BK * (kTileT + PAD), "prefixes fit the staging LDS");
+  auto put_pre = [&](int n, Pair m) {
+    pre[(2 * n) * (2 * kTileT) + tid] = m.u;
+    pre[(2 * n + 1) * (2 * kTileT) + tid] = m.v;
+  };
   Affine run = MinGRUOp::identity();
 #pragma unroll
   for (int n = 0; n < 8; ++n) {
@@ -133,9 +150,9 @@ void fused_proj_scan_kernel(const FusedParams F) {
                           __shfl_xor(mine[n].b, 32)};
     const Affine even = kl == 0 ? mine[n] : other;
     const Affine odd = kl == 0 ? other : mine[n];
-    if (kl == 0) pre[n] = MinGRUOp::map(run);
+    if (kl == 0) put_pre(n, MinGRUOp::map(run));
     run = MinGRUOp::compose(run, even);
-    if (kl == 1) pre[n] = MinGRUOp::map(run);
+    if (kl == 1) put_pre(n, MinGRUOp::map(run));
     run = MinGRUOp::compose(run, odd);
   }
   // 3. Wave rows along T, then the look-back across tiles.
@@ -143,20 +160,33 @@ void fused_proj_scan_kernel(const FusedParams F) {
   __syncthreads();
   resolve_tile<MinGRUOp, kTileT / 64, kTileD, 2 * kTileT, 2>(P, tl, s_pre, s_win, s_hin);
 
-  // 4. Replay and store.
+  // 4. Replay and store.  One buffer descriptor over the tile's rows of h:
+  // the lane's row and channel in the vector offset, the step's row within
+  // the lane's runs in the (wave-uniform) scalar offset, so that no 64-bit
+  // address per row is formed and kept across the look-back (the compiler
+  // had spilled 32 of them).  Rows past T are skipped explicitly: the range
+  // check does not cover the scalar offset.
   const float h_wave = MinGRUOp::apply(MinGRUOp::map(s_pre[wm][c]), s_hin[c]);
-  float* out = P.out + (tl.b * P.T + t0) * P.D + d;
+  const int64_t row_bytes = P.D * 4;
+  const rsrc_t ro = make_rsrc(P.out + (tl.b * P.T + t0) * P.D, rows * row_bytes);
+  const int vo = int((wm * 64 + kl * 4) * row_bytes + d * 4);
+  // The row that is step T - 1 (its state is h_T), relative to row_base, or
+  // -1 (no row of the lane's runs).
+  const int last_rel =
+      (P.last != nullptr && P.T - 1 - t0 < kTileT) ? int(P.T - 1 - t0) - row_base : -1;
 #pragma unroll
   for (int n = 0; n < 8; ++n) {
     const int i = n / 4, q = n % 4;
-    float h = MinGRUOp::apply(pre[n], h_wave);
+    const Pair pn = {pre[(2 * n) * (2 * kTileT) + tid], pre[(2 * n + 1) * (2 * kTileT) + tid]};
+    float h = MinGRUOp::apply(pn, h_wave);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int lr = wm * 64 + i * 32 + q * 8 + kl * 4 + j;
+      const int rel = i * 32 + q * 8 + j;  // the row is row_base + rel
       h = MinGRUOp::apply(Pair{acc[i][0][4 * q + j], acc[i][1][4 * q + j]}, h);
-      if (chan_ok && lr < rows) {
-        out[int64_t(lr) * P.D] = h;
-        if (P.last != nullptr && t0 + lr == P.T - 1) P.last[tl.b * P.D + d] = h;
+      if (chan_ok && rel < rows_rel) {
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(h), ro, vo, int(rel * row_bytes),
+                                              kStreamPolicy);
+        if (rel == last_rel) P.last[tl.b * P.D + d] = h;
       }
     }
   }
@@ -169,6 +199,8 @@ bool fused_forward_applies(int64_t B, int64_t T, int64_t D_h) {
   // problems keep the split-K projection, which spreads its K loop over more
   // workgroups.
   if (B <= 0 || T <= 0 || D_h <= 0) return false;
+  // A tile's rows of h are addressed with 32-bit byte offsets.
+  if (int64_t(kTileT) * D_h * 4 > int64_t(0x7FFFFFFF)) return false;
   const int64_t tiles = B * ((D_h + kTileD - 1) / kTileD) * ((T + kTileT - 1) / kTileT);
   return tiles >= 512 && tiles * 2 * kTileT <= int64_t(0xFFFFFFFFu);
 }
