@@ -35,7 +35,9 @@ carries:
                 Opt-in (name them in --legs): shapes -- one scan call over
                 the sweep shapes (both operators, bf16 and fp32 inputs);
                 streams -- read-only, write-only and read+write ceilings of
-                torch's own kernels on 2 GiB; placement -- the full-size
+                torch's own kernels on 2 GiB; step_sweep -- the decode
+                step's x_t W_in with the update (B=256, D_h=2048) over
+                D_in = 64 .. 4096, with a fixed + per-K fit; placement -- the full-size
                 backward (plain and decayed) and forward with their large
                 tensors carved from one buffer at chosen relative offsets.
 
@@ -594,6 +596,51 @@ def leg_shapes(torch, sr, synth, steps, warmup):
     return res
 
 
+def leg_step_sweep(torch, sr, synth, steps, warmup):
+    """The decode step's first product with the update (x_t W_in, then
+    h = h + z (g(p) - h); no output projection) at B=256, D_h=2048 over the
+    input width D_in: 32 launches captured in a HIP graph and replayed, so
+    that the host's per-call cost does not show; GPU time per launch from HIP
+    events around the replays (median over `steps` replays), and a
+    least-squares line through the points (fixed cost + cost per 1024 of K),
+    whose slope gives the K loop's share of the fp32 matrix peak."""
+    cfg = synth.CONFIGS[synth.STEP]
+    B, D_h = cfg["B"], cfg["D"]
+    res = {}
+    xs, ys = [], []
+    for D_in in (64, 128, 256, 512, 1024, 2048, 4096):
+        log(f"[bench] step sweep: D_in={D_in}")
+        W_in = torch.empty((D_in, 2 * D_h), device="cuda").normal_(0.0, D_in ** -0.5)
+        x = torch.empty((B, D_in), device="cuda").normal_(0.0, 1.0)
+        h = torch.zeros((B, D_h), device="cuda")
+        ws = torch.empty(max(sr.raw_library().mingru_step_workspace_size(B, D_in, D_h, D_h), 1),
+                         dtype=torch.uint8, device="cuda")
+        fn = lambda: sr.mingru_step(x, W_in, None, h_prev=h, h_next=h, workspace=ws)
+        per_graph = 32
+        for _ in range(3):
+            fn()  # the kernels' code loaded before the capture
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(per_graph):
+                fn()
+        med = median(time_launches(torch, graph.replay, steps, warmup)[1]) / per_graph
+        flops = 2.0 * B * D_in * 2 * D_h
+        res[f"d_in_{D_in}"] = {"launch_us_median": round(med * 1e3, 2),
+                               "frac_fp32_mfma": round(flops / (med * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4)}
+        xs.append(D_in / 1024.0)
+        ys.append(med * 1e3)
+        del graph, W_in, x, h, ws
+    n = len(xs)
+    mx, my = sum(xs) / n, sum(ys) / n
+    slope = sum((a - mx) * (b - my) for a, b in zip(xs, ys)) / sum((a - mx) ** 2 for a in xs)
+    flops_per_1024 = 2.0 * B * 1024 * 2 * D_h
+    res["fit"] = {"fixed_us": round(my - slope * mx, 2), "us_per_1024_k": round(slope, 2),
+                  "k_loop_frac_fp32_mfma": round(flops_per_1024 / (slope * 1e-6) / 1e12 /
+                                                 FP32_MFMA_PEAK_TFLOPS, 4)}
+    return res
+
+
 # Relative placements of the placement leg: each tensor's base moves by this
 # many bytes beyond the end of the previous one (0: bases 1-2 GiB apart).
 PLACEMENT_SHIFTS = [("packed", 0), ("each_+256B", 256), ("each_+64KiB", 64 << 10),
@@ -754,6 +801,8 @@ def main():
         extra["scan_shapes"] = leg_shapes(torch, sr, synth, 20, 5)
     if "streams" in legs:
         extra["stream_ceilings"] = leg_streams(torch)
+    if "step_sweep" in legs:
+        extra["step_sweep_b256_dh2048"] = leg_step_sweep(torch, sr, synth, 30, 5)
     if "placement" in legs:
         extra["placement_b8_t65536_d1024"] = leg_placement(torch, sr, synth, 40, 60)
     if "copy" in legs:
