@@ -184,8 +184,9 @@ void fused_proj_scan_kernel(const FusedParams F) {
       const int rel = i * 32 + q * 8 + j;  // the row is row_base + rel
       h = MinGRUOp::apply(Pair{acc[i][0][4 * q + j], acc[i][1][4 * q + j]}, h);
       if (chan_ok && rel < rows_rel) {
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(h), ro, vo, int(rel * row_bytes),
-                                              kStreamPolicy);
+        // Default cache policy (not streaming): the output projection that
+        // usually follows reads h, and mid-sized h stays in the Infinity Cache.
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(h), ro, vo, int(rel * row_bytes), 0);
         if (rel == last_rel) P.last[tl.b * P.D + d] = h;
       }
     }
