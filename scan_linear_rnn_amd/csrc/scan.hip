@@ -33,7 +33,8 @@
 //     look-back with a window); the nearest published end state, followed by
 //     the maps of the tiles after it, gives the state entering the tile.
 //     Only if the window holds no usable end state does the thread walk back
-//     one tile at a time.  The tile's end state is then published.
+//     further, a few words per round trip.  The tile's end state is then
+//     published.
 //   * Phase 3 (all waves): each lane starts from the state entering its run
 //     and re-applies its register-resident maps, storing h (or x) per step.
 //
